@@ -1,0 +1,9 @@
+"""CPU oracle for the exact-attention forward pass.
+
+Test infrastructure only: imported by tests/, the smoke check and the benchmark's
+CPU-baseline leg, never by the library or its Python binding.
+"""
+
+from .attention import attention_bruteforce, attention_ref, kv_head_of
+
+__all__ = ["attention_ref", "attention_bruteforce", "kv_head_of"]
