@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Forward-attention throughput on one MI355X: TFLOPS and fraction of the dense bf16 MFMA peak.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--causal] [--no-sweep]
+
+A step is one forward pass (one fa_fwd launch) over the named workload, inputs already
+resident in HBM. FLOPs = 4*B*Hq*Nq*Nk*d, halved for causal. Prints ONE JSON line on stdout;
+a table of the head_dim 128/256 sweep goes to stderr (and into the JSON as "sweep").
+
+The CPU baseline is the fp64 oracle timed on this host's cores over a bounded sample of
+query rows of the same workload (a reported baseline, not the target).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA peak (published)
+DEFAULT_WORKLOAD = "hd256_N8192"
+PAGES_B200 = {  # pages' own forward TFLOPS for the hd256 snapshot workloads (B200, context only)
+    ("hd256_N1024", False): 950, ("hd256_N2048", False): 1280, ("hd256_N4096", False): 1477,
+    ("hd256_N8192", False): 1594, ("hd256_N16384", False): 1663, ("hd256_N32768", False): 1709,
+    ("hd256_N65536", False): 1562, ("hd256_N131072", False): 1481,
+    ("hd256_N1024", True): 584, ("hd256_N2048", True): 897, ("hd256_N4096", True): 1191,
+    ("hd256_N8192", True): 1385, ("hd256_N16384", True): 1505, ("hd256_N32768", True): 1589,
+    ("hd256_N65536", True): 1594, ("hd256_N131072", True): 1457,
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    cdir = os.path.join(ROOT, "exact_attention_06_amd", "csrc")
+    for n in sorted(os.listdir(cdir)):
+        with open(os.path.join(cdir, n), "rb") as f:
+            h.update(n.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def gpu_inputs(w, torch):
+    """Seeded N(0,1) draws made on the GPU (same recipe as the CPU generator: fp32 normal,
+    rounded to bf16, optional x4 on every 16th key); used for timing only."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    dev = "cuda"
+    q = torch.randn((w.B, w.N, w.Hq, w.d), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((w.B, w.N, w.Hkv, w.d), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((w.B, w.N, w.Hkv, w.d), generator=g, device=dev).to(torch.bfloat16)
+    if w.k_spike:
+        k[:, 0::16] *= 4
+    return q, k, v
+
+
+def time_forward(fa, torch, q, k, v, causal, scale, steps, warmup):
+    """Returns (ms_per_step, per-launch ms list) with HIP events on the launch stream."""
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fa.forward(q, k, v, causal=causal, scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        fa.forward(q, k, v, causal=causal, scale=scale, out=out, lse=lse)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    total = evs[0].elapsed_time(evs[-1])
+    return total / steps, per
+
+
+def cpu_baseline(w, causal, budget_s=15.0):
+    """Time the fp64 oracle on a bounded sample of query rows of workload w."""
+    import numpy as np
+    import torch
+
+    from exact_attention_06_amd import workloads as W
+    from oracle import attention_ref
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    # sample: the first `nb` (b, h) pairs' key/value heads with R query rows each
+    q, k, v = W.make_qkv(1, w.N, w.N, w.Hq, w.Hkv, w.d, w.seed, k_spike=w.k_spike)
+    rows_all = W.sample_rows(1, w.Hq, w.N, w.seed).numpy()
+    R = rows_all.shape[2]
+    t0 = time.perf_counter()
+    done_rows = 0
+    flops = 0.0
+    for h in range(w.Hq):
+        sl = slice(h, h + 1)
+        kvh = h // (w.Hq // w.Hkv)
+        rows = rows_all[:, sl]
+        attention_ref(q[:, :, sl], k[:, :, kvh:kvh + 1], v[:, :, kvh:kvh + 1], causal, w.scale, rows=rows)
+        done_rows += R
+        vis = (rows[0, 0] + 1) if causal else np.full(R, w.N)
+        flops += float(np.sum(4.0 * vis * w.d))
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done_rows} sampled query rows ({R} per head, {done_rows // R} of {w.Hq} heads, batch 0) "
+                      f"of {w.name} {'causal' if causal else 'non-causal'}, all {w.N} keys, fp64 numpy; "
+                      f"{dt:.1f} s; FLOPs 4*d*visible_keys per row"}
+
+
+def load_traffic(kernel_name):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    e = rec.get(kernel_name)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--causal", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--sweep-steps", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_06_amd as fa
+    from exact_attention_06_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    w = W.by_name(args.workload)
+    causal = bool(args.causal)
+    q, k, v = gpu_inputs(w, torch)
+    torch.cuda.synchronize()
+    ms, per = time_forward(fa, torch, q, k, v, causal, w.scale, args.steps, args.warmup)
+    flops = w.flops(causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    avg_launch_ms = sum(per) / len(per)
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    del q, k, v
+    torch.cuda.empty_cache()
+    log(f"[bench] {w.name} causal={causal}: {ms:.3f} ms/step, {tflops:.1f} TFLOPS "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS:.0f})")
+
+    sweep = []
+    if not args.no_sweep:
+        pts = [x for x in W.hd128_sweep() + W.hd256_sweep()]
+        for x in pts:
+            qx, kx, vx = gpu_inputs(x, torch)
+            for c in (False, True):
+                m, _ = time_forward(fa, torch, qx, kx, vx, c, x.scale, args.sweep_steps, 2)
+                t = x.flops(c) / (m * 1e-3) / 1e12
+                ent = {"workload": x.name, "causal": c, "B": x.B, "N": x.N, "Hq": x.Hq, "Hkv": x.Hkv,
+                       "d": x.d, "ms": round(m, 4), "tflops": round(t, 1),
+                       "frac_peak": round(t / PEAK_BF16_TFLOPS, 4)}
+                b200 = PAGES_B200.get((x.name, c))
+                if b200:
+                    ent["pages_b200_tflops"] = b200
+                sweep.append(ent)
+                log(f"[sweep] {x.name:20s} {'causal' if c else 'noncausal':9s} {m:8.3f} ms "
+                    f"{t:7.1f} TFLOPS {100 * t / PEAK_BF16_TFLOPS:5.1f}%")
+            del qx, kx, vx
+            torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, causal)
+    if cpu:
+        log(f"[cpu] oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    kname = f"fwd_kernel<{w.d},{'causal' if causal else 'noncausal'},bf16>"
+    b200 = PAGES_B200.get((w.name, causal))
+    rec = {
+        "metric": "fwd attention TFLOPS + % of MI355X bf16 MFMA peak, hd128/hd256 at N=1k-128k",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tflops / b200, 4) if b200 else None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) fp32 draws rounded to bf16",
+        "config": {"workload": w.name, "B": w.B, "Nq": w.N, "Nk": w.N, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "d": w.d, "causal": causal, "scale": w.scale, "tokens": w.B * w.N,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(kname), "kernel": kname,
+                     "avg_launch_ms": round(avg_launch_ms, 4),
+                     "flops_per_launch": flops},
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if b200:
+        rec["vs_baseline_note"] = (f"ratio to the pages' B200 figure for this workload ({b200} TFLOPS, "
+                                   "another machine: context, not the target)")
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

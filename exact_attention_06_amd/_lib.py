@@ -1,0 +1,61 @@
+"""ctypes loader for libfa.so (the HIP library behind include/fa_fwd.h).
+
+Argument marshalling only: every step of the forward pass runs in the library's kernels.
+There is no fallback: if the library is missing, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfa.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "fa_fwd.h")
+
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_SHAPE = -2
+FA_ERR_HEADDIM = -3
+FA_ERR_CAUSAL_SHAPE = -4
+FA_ERR_SCALE = -5
+FA_ERR_ALIGN = -6
+FA_ERR_TOO_LARGE = -7
+FA_ERR_LAUNCH = -8
+
+_lib = None
+
+_I = ctypes.c_int
+_P = ctypes.c_void_p
+_FWD_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+_CHECK_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float]
+
+
+def load():
+    """Load libfa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_attention_06_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name in ("fa_fwd", "fa_fwd_f16"):
+            fn = getattr(lib, name)
+            fn.argtypes = _FWD_ARGS
+            fn.restype = _I
+        lib.fa_fwd_check.argtypes = _CHECK_ARGS
+        lib.fa_fwd_check.restype = _I
+        lib.fa_strerror.argtypes = [_I]
+        lib.fa_strerror.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load().fa_strerror(int(code)).decode()
+
+
+def header_symbols():
+    """Function names declared in include/fa_fwd.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fa_\w+)\s*\(", text, flags=re.M)))

@@ -1,0 +1,120 @@
+// fa_fwd.hip - host side of the C ABI declared in include/fa_fwd.h: argument checks,
+// compile-time kernel selection (head dim x causal x element type) and the launch.
+// Every check runs before the first HIP call; there is no fallback kernel.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "fa_fwd.h"
+#include "fa_kernel.h"
+
+namespace {
+
+// Tile configuration per head dim: waves per workgroup and keys per K/V tile.
+template <int D> struct Cfg;
+template <> struct Cfg<128> { static constexpr int NW = 4, BC = 64; };
+template <> struct Cfg<256> { static constexpr int NW = 4, BC = 32; };
+
+template <int D>
+constexpr int lds_bytes() { return 2 * 2 * Cfg<D>::BC * D * 2; }
+
+template <int D, bool CAUSAL, class T>
+int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
+  constexpr int NW = Cfg<D>::NW, BC = Cfg<D>::BC;
+  auto kern = fa::fwd_kernel<D, NW, BC, CAUSAL, T>;
+  constexpr int lds = lds_bytes<D>();
+  if (lds > 65536) {
+    static bool attr_set = false;  // idempotent; a race only repeats the same call
+    if (!attr_set) {
+      if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
+          hipSuccess)
+        return FA_ERR_LAUNCH;
+      attr_set = true;
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, stream, prm);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int D> int br() { return Cfg<D>::NW * 32; }
+
+int check(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+          int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (d != 128 && d != 256) return FA_ERR_HEADDIM;
+  if (causal && Nq != Nk) return FA_ERR_CAUSAL_SHAPE;
+  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
+  if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
+  const int64_t BR = d == 128 ? br<128>() : br<256>();
+  const int64_t nqt = (Nq + BR - 1) / BR;
+  const int64_t grid = (int64_t)B * Hq * nqt;
+  if (grid > INT_MAX || (int64_t)Nq + BR > INT_MAX || (int64_t)Nk + 256 > INT_MAX) return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+template <class T>
+int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq, int Nk,
+        int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  const int st = check(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale);
+  if (st != FA_OK) return st;
+  fa::FwdParams prm;
+  prm.q = (const uint8_t*)q;
+  prm.k = (const uint8_t*)k;
+  prm.v = (const uint8_t*)v;
+  prm.o = (uint8_t*)o;
+  prm.lse = lse;
+  prm.B = B;
+  prm.Nq = Nq;
+  prm.Nk = Nk;
+  prm.Hq = Hq;
+  prm.Hkv = Hkv;
+  prm.group = Hq / Hkv;
+  prm.c = scale * fa::LOG2E;
+  const int BR = d == 128 ? br<128>() : br<256>();
+  prm.nqt = (Nq + BR - 1) / BR;
+  const int grid = B * Hq * prm.nqt;
+  hipStream_t s = (hipStream_t)stream;
+  if (d == 128)
+    return causal ? launch<128, true, T>(prm, grid, s) : launch<128, false, T>(prm, grid, s);
+  return causal ? launch<256, true, T>(prm, grid, s) : launch<256, false, T>(prm, grid, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+                 int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale) {
+  return check(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale);
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq, int Nk,
+           int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  return run<fa::Bf16>(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale, stream);
+}
+
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq,
+               int Nk, int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  return run<fa::F16>(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale, stream);
+}
+
+const char* fa_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a pointer argument is NULL";
+    case FA_ERR_SHAPE: return "B, Nq, Nk, Hq and Hkv must be positive and Hq a multiple of Hkv";
+    case FA_ERR_HEADDIM: return "head dim must be 128 or 256";
+    case FA_ERR_CAUSAL_SHAPE: return "causal attention needs Nq == Nk";
+    case FA_ERR_SCALE: return "scale must be finite and non-negative";
+    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_TOO_LARGE: return "problem too large for 32-bit grid or sequence indexing";
+    case FA_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown fa status code";
+  }
+}
+
+}  // extern "C"

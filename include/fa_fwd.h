@@ -1,0 +1,84 @@
+/*
+ * fa_fwd.h - C ABI of the MI355X (gfx950) exact-attention forward library (libfa.so).
+ *
+ * The operation (softmax attention, computed tile by tile with an online softmax so the
+ * Nq x Nk score matrix never reaches device memory):
+ *
+ *   for every batch b and query head h, with kv head  kvh = h / (Hq / Hkv):
+ *     S[i][j]  = scale * dot(Q[b,i,h,:], K[b,j,kvh,:])
+ *     causal:  S[i][j] = -inf for j > i   (query i sees keys 0..i)
+ *     O[b,i,h,:]  = sum_j softmax_j(S[i][:]) * V[b,j,kvh,:]
+ *     LSE[b,h,i]  = ln( sum_j exp(S[i][j]) )
+ *
+ * Where each part is stated:
+ *   - the attention product and its tile-by-tile, running-max/running-sum evaluation:
+ *     "FlashAttention 4: Snellere, Geheugenefficiente Aandacht voor LLM's", sections
+ *     "Inleiding" and "Waarom aandachtkernels nog steeds de kosten van LLM's domineren";
+ *   - the native [batch, sequence, heads, head_dim] layout with matching FP16/BF16 Q/K/V
+ *     and an error (never a silent kernel change) on any contract violation:
+ *     "h3-blackwell-runtime/FLASH4.md", section "API";
+ *   - head_dim 256 next to 128, causal and non-causal variants: "[RFC] FA4 - head_dim=256 &
+ *     head_dim=512", sections "Overview" and "Performance Snapshot";
+ *   - grouped-query heads sharing one K/V head: the Dutch page's compatibility section.
+ *   The pages never define the LSE output; it is the natural-log log-sum-exp of the scaled
+ *   scores over the visible keys, in fp32.
+ *
+ * Layouts (all row-major, contiguous, element type bf16 for fa_fwd and fp16 for fa_fwd_f16):
+ *   q   [B, Nq, Hq,  d]        k, v  [B, Nk, Hkv, d]        o  [B, Nq, Hq, d]
+ *   lse [B, Hq, Nq] float32
+ *
+ * Ownership: every pointer is device memory owned by the caller. The library allocates
+ * nothing, keeps no state between calls and is re-entrant; concurrent calls on different
+ * streams are independent.
+ *
+ * Execution: asynchronous on `stream` (a hipStream_t; NULL means the default stream). The
+ * call never synchronises. Kernel faults surface at the caller's next synchronisation.
+ *
+ * Errors: 0 (FA_OK) or a negative FA_ERR_* code. Every argument check runs on the host
+ * before any HIP call, so invalid arguments never reach the GPU. There is no fallback path.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,         /* a pointer argument is NULL                                  */
+  FA_ERR_SHAPE = -2,        /* B, Nq, Nk, Hq or Hkv <= 0, or Hq % Hkv != 0                 */
+  FA_ERR_HEADDIM = -3,      /* d is not 128 or 256                                         */
+  FA_ERR_CAUSAL_SHAPE = -4, /* causal with Nq != Nk (the causal alignment is defined for
+                               square problems only)                                       */
+  FA_ERR_SCALE = -5,        /* scale is NaN, infinite or negative                          */
+  FA_ERR_ALIGN = -6,        /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+  FA_ERR_TOO_LARGE = -7,    /* the work grid or a per-head extent exceeds 2^31 - 1         */
+  FA_ERR_LAUNCH = -8        /* the HIP launch reported an error                            */
+};
+
+/* Forward pass, bf16 q/k/v/o, fp32 LSE. Arguments as described above; `scale` multiplies
+ * the q.k dot products (1/sqrt(d) is the usual choice). Returns an fa_status. */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
+           void* stream);
+
+/* Same as fa_fwd with fp16 q/k/v/o. */
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
+               void* stream);
+
+/* Static, NUL-terminated description of an fa_status code (never NULL). */
+const char* fa_strerror(int code);
+
+/* Host-only argument check shared by both entry points: returns the fa_status that
+ * fa_fwd would return for these arguments before launching anything (FA_OK when the
+ * launch would proceed). Makes no HIP call. */
+int fa_fwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

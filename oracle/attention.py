@@ -64,6 +64,21 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
+def torch_index(a: np.ndarray):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a))
+
+
+def _slice_f64(x, b, rows, h) -> np.ndarray:
+    """x[b, rows, h, :] as float64 (exact for bf16/fp16/fp32 inputs)."""
+    if hasattr(x, "detach"):  # torch tensor: slice first, then widen
+        if isinstance(rows, np.ndarray):
+            rows = torch_index(rows)
+        return x[b, rows, h, :].detach().cpu().double().numpy()
+    return np.asarray(x[b, rows, h, :], dtype=np.float64)
+
+
 def attention_ref(q, k, v, causal: bool, scale: float, rows=None):
     """Exact attention forward in float64.
 
@@ -73,13 +88,11 @@ def attention_ref(q, k, v, causal: bool, scale: float, rows=None):
     Returns (O, LSE) as float64 numpy arrays:
       rows is None: O [B, Nq, Hq, d], LSE [B, Hq, Nq]
       rows given:   O [B, Hq, R, d],  LSE [B, Hq, R]
+    Inputs are widened to float64 one (b, head) slice at a time.
     """
-    q = _as_f64(q)
-    k = _as_f64(k)
-    v = _as_f64(v)
     B, Nq, Hq, d = q.shape
     Bk, Nk, Hkv, dk = k.shape
-    if Bk != B or dk != d or v.shape != k.shape:
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
         raise ValueError("q/k/v shapes do not agree")
     if causal and Nq != Nk:
         raise ValueError("causal attention is defined here for Nq == Nk only")
@@ -96,13 +109,16 @@ def attention_ref(q, k, v, causal: bool, scale: float, rows=None):
         O = np.empty((B, Hq, R, d), dtype=np.float64)
         LSE = np.empty((B, Hq, R), dtype=np.float64)
 
+    all_k = slice(None)
     for b in range(B):
+        cached = None
         for h in range(Hq):
             kvh = kv_head_of(h, Hq, Hkv)
-            Kh = k[b, :, kvh, :]  # [Nk, d]
-            Vh = v[b, :, kvh, :]  # [Nk, d]
+            if cached is None or cached[0] != kvh:
+                cached = (kvh, _slice_f64(k, b, all_k, kvh), _slice_f64(v, b, all_k, kvh))
+            _, Kh, Vh = cached  # [Nk, d] each
             qi = np.arange(Nq) if rows is None else rows[b, h]
-            Qh = q[b, qi, h, :]  # [R, d]
+            Qh = _slice_f64(q, b, all_k if rows is None else qi, h)  # [R, d]
             S = scale * (Qh @ Kh.T)  # [R, Nk]
             if causal:
                 S[np.arange(Nk)[None, :] > qi[:, None]] = -np.inf

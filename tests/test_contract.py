@@ -1,0 +1,118 @@
+"""Boundary contract (CPU only): the library loads, exports what include/fa_fwd.h declares,
+and rejects every invalid argument on the host before any HIP call. The strict-backend
+rule comes from "h3-blackwell-runtime/FLASH4.md", section "API": matching FP16/BF16
+tensors, matching shapes, a supported head dim, and an error instead of a kernel change.
+"""
+
+import ctypes
+import math
+
+import pytest
+import torch
+
+import exact_attention_06_amd as fa
+from exact_attention_06_amd import _lib
+
+A = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced by the checks
+GOOD = dict(q=A, k=A + 0x100, v=A + 0x200, o=A + 0x300, lse=A + 0x400, B=2, Nq=300, Nk=300,
+            Hq=8, Hkv=2, d=128, causal=0, scale=0.0884)
+
+
+def _check(**kw):
+    a = dict(GOOD, **kw)
+    return fa.check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Nq"], a["Nk"], a["Hq"],
+                         a["Hkv"], a["d"], a["causal"], a["scale"])
+
+
+def _fwd(fn, **kw):
+    a = dict(GOOD, **kw)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Nq"], a["Nk"], a["Hq"], a["Hkv"],
+              a["d"], a["causal"], ctypes.c_float(a["scale"]), None)
+
+
+def test_library_exports_every_header_symbol():
+    lib = _lib.load()
+    names = _lib.header_symbols()
+    assert set(names) == {"fa_fwd", "fa_fwd_f16", "fa_strerror", "fa_fwd_check"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_valid_arguments_pass():
+    assert _check() == _lib.FA_OK
+    assert _check(d=256, causal=1, Hkv=8) == _lib.FA_OK
+    assert _check(Nq=1, Nk=1) == _lib.FA_OK
+    assert _check(Nq=5, Nk=9000) == _lib.FA_OK
+    assert _check(scale=0.0) == _lib.FA_OK
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_null_pointer(field):
+    assert _check(**{field: 0}) == _lib.FA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0), dict(Nk=-1), dict(Hq=0), dict(Hkv=0),
+                                dict(Hq=8, Hkv=3), dict(Hq=2, Hkv=4)])
+def test_bad_shape(kw):
+    assert _check(**kw) == _lib.FA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("d", [0, 64, 96, 127, 192, 512])
+def test_bad_head_dim(d):
+    assert _check(d=d) == _lib.FA_ERR_HEADDIM
+
+
+def test_causal_needs_square():
+    assert _check(causal=1, Nq=300, Nk=301) == _lib.FA_ERR_CAUSAL_SHAPE
+    assert _check(causal=0, Nq=300, Nk=301) == _lib.FA_OK
+
+
+@pytest.mark.parametrize("s", [math.inf, -math.inf, math.nan, -0.5])
+def test_bad_scale(s):
+    assert _check(scale=s) == _lib.FA_ERR_SCALE
+
+
+@pytest.mark.parametrize("kw", [dict(q=A + 8), dict(k=A + 2), dict(v=A + 4), dict(o=A + 1), dict(lse=A + 2)])
+def test_misaligned(kw):
+    assert _check(**kw) == _lib.FA_ERR_ALIGN
+
+
+def test_lse_4_byte_alignment_is_enough():
+    assert _check(lse=A + 4) == _lib.FA_OK
+
+
+def test_too_large_grid():
+    assert _check(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 12, Nk=1 << 12) == _lib.FA_ERR_TOO_LARGE
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f16"])
+def test_entry_points_reject_before_any_hip_call(entry):
+    # These calls must return on the host; with no GPU present a HIP call would fail differently.
+    fn = getattr(_lib.load(), entry)
+    assert _fwd(fn, q=0) == _lib.FA_ERR_NULL
+    assert _fwd(fn, d=64) == _lib.FA_ERR_HEADDIM
+    assert _fwd(fn, causal=1, Nk=17) == _lib.FA_ERR_CAUSAL_SHAPE
+    assert _fwd(fn, Hkv=3) == _lib.FA_ERR_SHAPE
+    assert _fwd(fn, scale=math.nan) == _lib.FA_ERR_SCALE
+    assert _fwd(fn, o=A + 2) == _lib.FA_ERR_ALIGN
+
+
+def test_strerror_covers_codes():
+    seen = set()
+    for code in range(-8, 1):
+        msg = _lib.strerror(code)
+        assert msg and msg != "unknown fa status code"
+        seen.add(msg)
+    assert len(seen) == 9
+    assert _lib.strerror(-99) == "unknown fa status code"
+
+
+def test_python_layer_rejects_cpu_tensors():
+    q = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward(q, q, q)
+
+
+def test_python_layer_error_type():
+    err = fa.FaError(_lib.FA_ERR_HEADDIM, _lib.strerror(_lib.FA_ERR_HEADDIM))
+    assert isinstance(err, ValueError) and "head dim" in str(err)
