@@ -24,6 +24,8 @@ HIPCC_FLAGS = [
     "-fPIC",
     # keep packed fp32 VALU ops out of every code object
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs (the online-softmax rescale touches them with VALU ops)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
     "-I", os.path.join(PKG, "csrc"),
 ]

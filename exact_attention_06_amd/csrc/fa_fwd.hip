@@ -12,21 +12,14 @@
 
 namespace {
 
-// Tile configuration per head dim: waves per workgroup and keys per K/V tile.
-template <int D> struct Cfg;
-template <> struct Cfg<128> { static constexpr int NW = 4, BC = 64; };
-template <> struct Cfg<256> { static constexpr int NW = 4, BC = 32; };
-
-template <int D>
-constexpr int lds_bytes() { return 2 * 2 * Cfg<D>::BC * D * 2; }
-
 template <int D, bool CAUSAL, class T>
 int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
-  constexpr int NW = Cfg<D>::NW, BC = Cfg<D>::BC;
-  auto kern = fa::fwd_kernel<D, NW, BC, CAUSAL, T>;
-  constexpr int lds = lds_bytes<D>();
+  using L = fa::Layout<D>;
+  auto kern = fa::fwd_kernel<D, CAUSAL, T>;
+  constexpr int lds = L::LDS;
   if (lds > 65536) {
-    static bool attr_set = false;  // idempotent; a race only repeats the same call
+    // Raising the dynamic LDS limit is idempotent; a race between threads only repeats it.
+    static bool attr_set = false;
     if (!attr_set) {
       if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
           hipSuccess)
@@ -34,11 +27,11 @@ int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
       attr_set = true;
     }
   }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, stream, prm);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(L::NW * 64), lds, stream, prm);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-template <int D> int br() { return Cfg<D>::NW * 32; }
+template <int D> int br() { return fa::Layout<D>::BR; }
 
 int check(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
           int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale) {

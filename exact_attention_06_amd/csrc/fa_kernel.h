@@ -17,8 +17,13 @@
 //     scalar, and P^T feeds the second MFMA's B operand straight from registers;
 //   * V^T is read with ds_read_b64_tr_b16 (LDS transpose read), so V stays in its natural
 //     [key][d] layout in LDS;
-//   * K/V tiles are double-buffered in LDS with an XOR swizzle of 16-byte chunks; the next
-//     tile's global loads are issued before the current tile's math;
+//   * K/V tiles are double-buffered in LDS; rows are padded (K by 16 B, V by 32 B) so that
+//     the 16-byte K reads of 16 consecutive rows and the 4-row transpose reads of V hit
+//     distinct banks, and every LDS read address is one per-lane base plus an immediate;
+//   * software pipeline inside each wave: while the softmax of tile j runs on the VALU,
+//     the score MFMAs of tile j+1 are in flight; then the P.V MFMAs of tile j. K(j+2) and
+//     V(j+1) are loaded at the top of iteration j by buffer loads that write LDS directly
+//     (no staging registers) and whose range check returns zeros past the last key;
 //   * softmax in base 2: p = exp2(s*c - m), c = scale*log2(e), on v_exp_f32;
 //   * lazy rescale: the running max m (log2 units) is raised only when some row of the
 //     wave sees a tile max above m + TAU; until then p <= 2^TAU;
@@ -35,6 +40,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
@@ -54,8 +60,8 @@ struct Bf16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ x2 cvt2(float a, float b) {
-    x2 r = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32, round to nearest even
-    return r;
+    f32x2 f = {a, b};
+    return __builtin_convertvector(f, x2);  // one v_cvt_pk_bf16_f32, round to nearest even
   }
   static __device__ __forceinline__ float dot2(x2 a, x2 b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
@@ -73,8 +79,8 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ x2 cvt2(float a, float b) {
-    x2 r = {(_Float16)a, (_Float16)b};
-    return r;
+    f32x2 f = {a, b};
+    return __builtin_convertvector(f, x2);
   }
   static __device__ __forceinline__ float dot2(x2 a, x2 b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
@@ -98,11 +104,15 @@ struct FwdParams {
 };
 
 template <bool V> struct BoolC { static constexpr bool value = V; };
+template <int V> struct IntC { static constexpr int value = V; };
 
-// XOR swizzle of the 16-byte chunk index inside an LDS row: 16 consecutive rows map one
-// logical chunk to 16 different physical chunks (GEMM1 reads), and the 4-row groups read
-// by ds_read_b64_tr_b16 land in 4 different chunk pairs.
-__device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+// Lane l and lane l^32 hold the same query row: the value of the other half.
+__device__ __forceinline__ float other_half(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  // v_permlane32_swap: r[0] = lanes 0-31 of x in both halves, r[1] = lanes 32-63 of x
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (__lane_id() >> 5) ? r[0] : r[1]);
+}
 
 // Block id -> (b*Hq + h, query tile). Workgroups are dispatched round-robin over the 8
 // XCDs (bid % 8); when B*Hq is a multiple of 8, each XCD gets a contiguous set of heads so
@@ -131,25 +141,49 @@ __device__ __forceinline__ void decode_block(int bid, const FwdParams& p, int& b
   }
 }
 
-template <int D, int NW, int BC, bool CAUSAL, class T>
-__global__ void __launch_bounds__(NW * 64)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
+  // raw buffer (stride 0): a load whose offset lies past `bytes` returns zeros
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// Tile configuration per head dim: waves per workgroup, keys per K/V tile.
+template <int D> struct TileCfg;
+template <> struct TileCfg<128> { static constexpr int NW = 8, BC = 64; };
+template <> struct TileCfg<256> { static constexpr int NW = 4, BC = 32; };
+
+template <int D>
+struct Layout {
+  static constexpr int NW = TileCfg<D>::NW, BC = TileCfg<D>::BC;
+  static constexpr int BR = NW * 32;           // query rows per workgroup
+  static constexpr int KROW = D * 2 + 16;      // padded LDS row pitch of K (bytes)
+  static constexpr int VROW = D * 2 + 32;      // padded LDS row pitch of V (bytes)
+  static constexpr int KT = BC * KROW;         // bytes per K tile
+  static constexpr int VT = BC * VROW;         // bytes per V tile
+  static constexpr int LDS = 2 * KT + 2 * VT;  // [K0][K1][V0][V1]
+};
+
+template <int D, bool CAUSAL, class T>
+__global__ void __launch_bounds__(TileCfg<D>::NW * 64)
 fwd_kernel(FwdParams p) {
   using x8 = typename T::x8;
   using x2 = typename T::x2;
+  using L = Layout<D>;
+  constexpr int NW = L::NW, BC = L::BC, BR = L::BR;
   constexpr int NT = NW * 64;
-  constexpr int BR = NW * 32;
   constexpr int KS1 = D / 16;       // GEMM1 k-steps (over head dim)
   constexpr int MT1 = BC / 32;      // score tiles (32 keys each) per K/V tile
   constexpr int MT2 = D / 32;       // output tiles (32 head-dim rows each)
   constexpr int KS2 = BC / 16;      // GEMM2 k-steps (over keys)
-  constexpr int ROWB = D * 2;       // bytes per K/V row in LDS
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int TILEB = BC * ROWB;  // bytes per K or V tile
-  constexpr int LOADS = BC * CPR / NT;
-  static_assert((BC * CPR) % NT == 0, "tile chunks must divide over the workgroup");
-  static_assert(BC % 32 == 0 && D % 32 == 0 && CPR >= 16, "tile shape");
+  constexpr int CPR = D / 8;        // 16-byte chunks per K/V row
+  constexpr int RPP = NT / CPR;     // rows staged per pass of the workgroup
+  constexpr int LOADS = BC / RPP;   // staging passes per tile
+  constexpr int KROW = L::KROW, VROW = L::VROW, KT = L::KT, VT = L::VT;
+  static_assert(NT % CPR == 0 && BC % RPP == 0, "tile chunks must divide over the workgroup");
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [2 buffers][K, V][TILEB]
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* const kbuf = smem;           // two K tiles
+  uint8_t* const vbuf = smem + 2 * KT;  // two V tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,6 +206,8 @@ fwd_kernel(FwdParams p) {
   int kend = Nk;
   if (CAUSAL) kend = min(Nk, min(Nq, q_wg0 + BR));
   const int ntiles = (kend + BC - 1) / BC;
+  // tiles this wave computes on (causal: keys up to its last query; at least tile 0)
+  const int wtiles = CAUSAL ? max(1, min(ntiles, (min(qw0 + 32, Nq) + BC - 1) / BC)) : ntiles;
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q_ld, dims 16t + 8hh .. +7
   x8 qf[KS1];
@@ -190,90 +226,127 @@ fwd_kernel(FwdParams p) {
   float m_run = -__builtin_inff();
   float lL = 0.f, lO = 0.f;
   const float c = p.c;
-
-  // ---- K/V staging: global -> registers -> LDS (swizzled)
-  const size_t kv_row = (size_t)p.Hkv * D * 2;  // bytes between consecutive tokens
-  const uint8_t* kbase = p.k + ((size_t)b * Nk * p.Hkv + kvh) * (size_t)(D * 2);
-  const uint8_t* vbase = p.v + ((size_t)b * Nk * p.Hkv + kvh) * (size_t)(D * 2);
-  u32x4 stK[LOADS], stV[LOADS];
-
-  auto gload = [&](int tile) {
-    const int k0 = tile * BC;
-#pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
-      const int pidx = tid + n * NT;
-      const int row = pidx / CPR, ch = pidx % CPR;
-      int key = k0 + row;
-      key = key < Nk ? key : Nk - 1;
-      const size_t off = (size_t)key * kv_row + ch * 16;
-      stK[n] = *(const u32x4*)(kbase + off);
-      stV[n] = *(const u32x4*)(vbase + off);
-    }
-  };
-  auto swrite = [&](int buf) {
-    uint8_t* kb = smem + buf * 2 * TILEB;
-#pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
-      const int pidx = tid + n * NT;
-      const int row = pidx / CPR, ch = pidx % CPR;
-      const int pos = row * ROWB + ((ch ^ swz(row)) << 4);
-      *(u32x4*)(kb + pos) = stK[n];
-      *(u32x4*)(kb + TILEB + pos) = stV[n];
-    }
-  };
-
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
   const x2 one2 = T::ones();
 
-  // One K/V tile of work for this wave. SPLIT_P (used on the wave's first tile): P is fed to
-  // the second product as hi + lo, two rounded parts whose sum carries ~16 significant bits,
-  // so rows that have seen only a few keys are not limited by the 8-bit rounding of P.
-  auto tile_step = [&](const int j, auto split_tag) {
-    constexpr bool SPLIT_P = decltype(split_tag)::value;
-    const int buf = j & 1;
-    const int k0 = j * BC;
-    const uint8_t* kl = smem + buf * 2 * TILEB;
-    const uint8_t* vl = kl + TILEB;
-    // ---- GEMM1: S^T[key][q] = sum_d K[key][d] Q[q][d]
-    f32x16 s[MT1];
+  // ---- K/V tiles: buffer loads straight into LDS (buffer_load ... lds). One instruction
+  //      of a wave fills 64 consecutive 16-byte LDS slots (M0 base + 16 * lane); a padded row
+  //      is KROW/16 (VROW/16) slots, so each lane maps its slot to (row, chunk) once, here.
+  //      Pad slots and rows past the last key get an offset beyond the buffer's range, which
+  //      loads zeros; lanes past the end of the tile are switched off. Every offset is in the
+  //      per-lane voffset, which is what the hardware range check covers.
+  constexpr int KSL = KROW / 16, VSL = VROW / 16;            // slots per padded row
+  constexpr int KI = (BC * KSL + 63) / 64, VI = (BC * VSL + 63) / 64;  // instructions per tile
+  constexpr int KPW = (KI + NW - 1) / NW, VPW = (VI + NW - 1) / NW;    // per wave (at most)
+  constexpr uint32_t OOB = 0x80000000u;
+  const uint32_t kv_row = (uint32_t)p.Hkv * D * 2;  // bytes between consecutive tokens
+  const uint8_t* kbase = p.k + ((size_t)b * Nk * p.Hkv + kvh) * (size_t)(D * 2);
+  const uint8_t* vbase = p.v + ((size_t)b * Nk * p.Hkv + kvh) * (size_t)(D * 2);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t k_vo[KPW], v_vo[VPW];
+#pragma unroll
+  for (int n = 0; n < KPW; ++n) {
+    const int slot = 64 * (wv + NW * n) + lane, row = slot / KSL, ch = slot % KSL;
+    k_vo[n] = (ch < CPR && row < BC) ? (uint32_t)row * kv_row + ch * 16 : OOB;
+  }
+#pragma unroll
+  for (int n = 0; n < VPW; ++n) {
+    const int slot = 64 * (wv + NW * n) + lane, row = slot / VSL, ch = slot % VSL;
+    v_vo[n] = (ch < CPR && row < BC) ? (uint32_t)row * kv_row + ch * 16 : OOB;
+  }
+
+  auto load_tile = [&](int tile, const uint8_t* gbase, uint8_t* ldst, const uint32_t* vo,
+                       auto ni_tag, auto sl_tag) {
+    constexpr int NI = decltype(ni_tag)::value, SL = decltype(sl_tag)::value;
+    const int k0 = tile * BC;
+    const uint32_t valid = (uint32_t)min(BC, Nk - k0) * kv_row;
+    const auto rs = make_rsrc(gbase + (size_t)k0 * kv_row, valid);
+#pragma unroll
+    for (int n = 0; n < (NI + NW - 1) / NW; ++n) {
+      const int I = wv + NW * n;
+      if (I < NI) {
+        if (64 * I + 64 <= BC * SL || 64 * I + lane < BC * SL)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(ldst + 1024 * I), 16, vo[n], 0, 0, 0);
+      }
+    }
+  };
+  auto load_k = [&](int tile, int buf) {
+    load_tile(tile, kbase, kbuf + buf * KT, k_vo, IntC<KI>{}, IntC<KSL>{});
+  };
+  auto load_v = [&](int tile, int buf) {
+    load_tile(tile, vbase, vbuf + buf * VT, v_vo, IntC<VI>{}, IntC<VSL>{});
+  };
+
+  // ---- per-lane LDS read bases
+  // GEMM1 A operand (K): lane reads row 32mt + l32, dims 16t + 8hh .. +7
+  const int k_rd = l32 * KROW + hh * 16;
+  // GEMM2 A operand (V^T) via ds_read_b64_tr_b16: k-step u covers keys
+  // 16u + {4g + 0..3, 8 + 4g + 0..3}, g = (lane group) / 2, which is the order P^T holds
+  // them in; lane i of a 16-lane group reads row key0 + i/4, dims d0 + 4(i%4) .. +3, and
+  // lane c of the group receives V[key0 + 0..3][d0 + c].
+  const int grp = lane >> 4, gi = lane & 15;
+  const int v_rd = (4 * (grp >> 1) + (gi >> 2)) * VROW + (2 * (grp & 1) + ((gi & 3) >> 1)) * 16 + (gi & 1) * 8;
+
+  auto gemm1 = [&](int buf, f32x16 (&s)[MT1]) {
+    const uint8_t* kl = kbuf + buf * KT + k_rd;
 #pragma unroll
     for (int mt = 0; mt < MT1; ++mt) {
       s[mt] = f32x16{};
-      const int row = mt * 32 + l32;
-      const uint8_t* rp = kl + row * ROWB;
-      const int sw = swz(row);
 #pragma unroll
       for (int t = 0; t < KS1; ++t) {
-        const int ch = (2 * t + hh) ^ sw;
-        u32x4 raw = *(const u32x4*)(rp + (ch << 4));
+        u32x4 raw = *(const u32x4*)(kl + mt * 32 * KROW + t * 32);
         s[mt] = T::mfma(__builtin_bit_cast(x8, raw), qf[t], s[mt]);
       }
     }
-    // ---- mask: causal (key > query) and tail (key >= Nk); lane's query is q_lane,
-    //      register r of score tile mt holds key k0 + 32mt + 8(r/4) + 4hh + r%4
-    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > qw0));
-    if (need_mask) {
+  };
+
+  auto gemm2 = [&](int buf, const x8 (&pf)[KS2], const x8* pl) {
+    const uint8_t* vl = vbuf + buf * VT + v_rd;
+#pragma unroll
+    for (int md = 0; md < MT2; ++md)
+#pragma unroll
+      for (int u = 0; u < KS2; ++u) {
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vl + (16 * u) * VROW + md * 64));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vl + (16 * u + 8) * VROW + md * 64));
+        u32x4 raw;
+        raw[0] = __builtin_bit_cast(u32x2, lo4)[0];
+        raw[1] = __builtin_bit_cast(u32x2, lo4)[1];
+        raw[2] = __builtin_bit_cast(u32x2, hi4)[0];
+        raw[3] = __builtin_bit_cast(u32x2, hi4)[1];
+        const x8 vfrag = __builtin_bit_cast(x8, raw);
+        acc[md] = T::mfma(vfrag, pf[u], acc[md]);
+        if (pl) acc[md] = T::mfma(vfrag, pl[u], acc[md]);
+      }
+  };
+
+  // Mask scores of tile j: causal (key > query) and tail (key >= Nk). Register r of score
+  // tile mt holds key k0 + 32mt + 8(r/4) + 4hh + r%4 for the lane's query q_lane, so a key
+  // is visible iff its compile-time offset 32mt + 8(r/4) + r%4 is <= one per-lane limit.
+  auto mask = [&](int j, f32x16 (&s)[MT1]) {
+    const int k0 = j * BC;
+    const bool need = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > qw0));
+    if (need) {
+      const int last = CAUSAL ? min(q_lane, Nk - 1) : Nk - 1;  // last visible key
+      const int lim = last - k0 - 4 * hh;
 #pragma unroll
       for (int mt = 0; mt < MT1; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool masked = (key >= Nk) || (CAUSAL && key > q_lane);
-          if (masked) s[mt][r] = -__builtin_inff();
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * mt + 8 * (r >> 2) + (r & 3) > lim) s[mt][r] = -__builtin_inff();
     }
-    // ---- row max (lane-local over its keys, then across the two lane halves)
+  };
+
+  // Row max of a tile and the lazy rescale of O and the sums (decided per wave).
+  auto max_rescale = [&](f32x16 (&s)[MT1]) {
     float mx = s[0][0];
 #pragma unroll
     for (int mt = 0; mt < MT1; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[mt][r]);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    mx = __builtin_fmaxf(mx, other_half(mx));
     const float mtile = mx * c;  // c >= 0, so max(s)*c == max(s*c)
-    // ---- lazy rescale, decided per wave
     const bool grow = mtile > m_run + TAU;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float mnew = __builtin_fmaxf(m_run, mtile);
@@ -284,10 +357,12 @@ fwd_kernel(FwdParams p) {
       lO *= alpha;
       m_run = mnew;
     }
-    // ---- p = exp2(s*c - m); P rounded to the MFMA element type; two row sums
+  };
+
+  // p = exp2(s*c - m), rounded to the MFMA type; lL += sum p (fp32), lO += sum of rounded p.
+  // With pl, also lo = round(p - hi), so hi + lo carries ~16 significant bits.
+  auto softmax = [&](const f32x16 (&s)[MT1], x8 (&pf)[KS2], x8* pl) {
     const float negm = -m_run;
-    x8 pf[KS2];
-    x8 pl[SPLIT_P ? KS2 : 1];
     float sumL = 0.f, sumO = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT1; ++mt)
@@ -301,7 +376,7 @@ fwd_kernel(FwdParams p) {
         const int u = mt * 2 + (r >> 3);
         pf[u][(r & 7)] = pb[0];
         pf[u][(r & 7) + 1] = pb[1];
-        if constexpr (SPLIT_P) {
+        if (pl) {
           const x2 lo = T::cvt2(p0 - (float)pb[0], p1 - (float)pb[1]);
           sumO = T::dot2(lo, one2, sumO);
           pl[u][(r & 7)] = lo[0];
@@ -310,56 +385,61 @@ fwd_kernel(FwdParams p) {
       }
     lL += sumL;
     lO += sumO;
-    // ---- GEMM2: O^T[d][q] += sum_key V^T[d][key] P^T[key][q]
-    // k-step u covers keys 16u + {4hh + 0..3, 8 + 4hh + 0..3} (the order P^T holds them).
-    // ds_read_b64_tr_b16: lane i of a 16-lane group reads row key0 + i/4, dims
-    // d0 + 4(i%4) .. +3; lane c of the group receives V[key0 + 0..3][d0 + c].
-    const int grp = lane >> 4, gi = lane & 15;
-    const int rsub = gi >> 2;                          // row inside the 4-row block
-    const int dsub = 2 * (grp & 1) + ((gi & 3) >> 1);  // 16-byte chunk inside 32 dims
-    const int half8 = (gi & 1) * 8;                    // byte offset inside the chunk
-#pragma unroll
-    for (int md = 0; md < MT2; ++md)
-#pragma unroll
-      for (int u = 0; u < KS2; ++u) {
-        s16x4 lo4, hi4;
-        {
-          const int row = 16 * u + 4 * (grp >> 1) + rsub;
-          const int ch = (4 * md + dsub) ^ swz(row);
-          lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + row * ROWB + (ch << 4) + half8));
-        }
-        {
-          const int row = 16 * u + 8 + 4 * (grp >> 1) + rsub;
-          const int ch = (4 * md + dsub) ^ swz(row);
-          hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + row * ROWB + (ch << 4) + half8));
-        }
-        u32x4 raw;
-        raw[0] = __builtin_bit_cast(u32x2, lo4)[0];
-        raw[1] = __builtin_bit_cast(u32x2, lo4)[1];
-        raw[2] = __builtin_bit_cast(u32x2, hi4)[0];
-        raw[3] = __builtin_bit_cast(u32x2, hi4)[1];
-        const x8 vfrag = __builtin_bit_cast(x8, raw);
-        acc[md] = T::mfma(vfrag, pf[u], acc[md]);
-        if constexpr (SPLIT_P) acc[md] = T::mfma(vfrag, pl[u], acc[md]);
-      }
   };
 
-  // tile 0 (never skipped: key 0 is visible to every query)
-  if (ntiles > 1) gload(1);
-  tile_step(0, BoolC<true>{});
-  if (ntiles > 1) swrite(1);
-  __syncthreads();
-  for (int j = 1; j < ntiles; ++j) {
-    if (j + 1 < ntiles) gload(j + 1);
-    const bool skip = CAUSAL && (j * BC > qw0 + 31);  // every key after every query of this wave
-    if (!skip) tile_step(j, BoolC<false>{});
-    if (j + 1 < ntiles) swrite((j + 1) & 1);
-    __syncthreads();
-  }
+  // ---- prologue: K(0), V(0), K(1) into LDS, scores of tile 0
+  load_k(0, 0);
+  load_v(0, 0);
+  if (ntiles > 1) load_k(1, 1);
+  __syncthreads();  // waits for the loads (vmcnt) before the barrier
+
+  f32x16 s_cur[MT1];
+  gemm1(0, s_cur);
+  __syncthreads();  // every wave has read K(0) before iteration 0 reloads its buffer
+
+  // ---- tile loop. Iteration j: loads of K(j+2), V(j+1) in flight; softmax(j) with the
+  //      MFMAs of GEMM1(j+1); GEMM2(j); the staged loads go to LDS; barrier.
+  //      Tiles below `nfull` are visible to every query of the workgroup and inside Nk, so
+  //      their iterations carry no masking code; the rest (diagonal and tail tiles) mask,
+  //      and a wave whose queries all precede a tile skips that tile's math.
+  int nfull = Nk / BC;
+  if (CAUSAL) nfull = min(nfull, (q_wg0 + 1) / BC);
+  auto iteration = [&](const int j, auto split_tag, auto mask_tag) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    constexpr bool MASKED = decltype(mask_tag)::value;
+    const bool more_k = j + 2 < ntiles, more_v = j + 1 < ntiles;
+    if (more_k) load_k(j + 2, j & 1);
+    if (more_v) load_v(j + 1, (j + 1) & 1);
+    const bool active = !MASKED || j < wtiles;
+    const bool next_active = MASKED ? (j + 1 < wtiles) : (j + 1 < ntiles);
+    f32x16 s_next[MT1];
+    if (active) {
+      if (MASKED) mask(j, s_cur);
+      max_rescale(s_cur);
+      x8 pf[KS2];
+      x8 pl[SPLIT ? KS2 : 1];
+      if (next_active) gemm1((j + 1) & 1, s_next);
+      softmax(s_cur, pf, SPLIT ? pl : nullptr);
+      gemm2(j & 1, pf, SPLIT ? pl : nullptr);
+    }
+    __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
+    if (next_active) {
+#pragma unroll
+      for (int mt = 0; mt < MT1; ++mt) s_cur[mt] = s_next[mt];
+    }
+  };
+
+  if (nfull > 0)
+    iteration(0, BoolC<true>{}, BoolC<false>{});
+  else
+    iteration(0, BoolC<true>{}, BoolC<true>{});
+  int j = 1;
+  for (; j < nfull; ++j) iteration(j, BoolC<false>{}, BoolC<false>{});
+  for (; j < ntiles; ++j) iteration(j, BoolC<false>{}, BoolC<true>{});
 
   // ---- epilogue: combine the two lane halves' sums, normalise, store O and LSE
-  lL += __shfl_xor(lL, 32);
-  lO += __shfl_xor(lO, 32);
+  lL += other_half(lL);
+  lO += other_half(lO);
   if (q_lane < Nq) {
     const float inv = 1.0f / lO;
     uint8_t* op = p.o + (((size_t)b * Nq + q_lane) * p.Hq + hq) * (size_t)(D * 2);
