@@ -15,19 +15,8 @@ namespace {
 template <int D, bool CAUSAL, class T>
 int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
   using L = fa::Layout<D>;
-  auto kern = fa::fwd_kernel<D, CAUSAL, T>;
-  constexpr int lds = L::LDS;
-  if (lds > 65536) {
-    // Raising the dynamic LDS limit is idempotent; a race between threads only repeats it.
-    static bool attr_set = false;
-    if (!attr_set) {
-      if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
-          hipSuccess)
-        return FA_ERR_LAUNCH;
-      attr_set = true;
-    }
-  }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(L::NW * 64), lds, stream, prm);
+  // the kernel's K/V buffers are static LDS (L::LDS bytes, within gfx950's 160 KB per CU)
+  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, T>), dim3(grid), dim3(L::NW * 64), 0, stream, prm);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -159,7 +159,7 @@ struct Layout {
   static constexpr int VROW = D * 2 + 32;      // padded LDS row pitch of V (bytes)
   static constexpr int KT = BC * KROW;         // bytes per K tile
   static constexpr int VT = BC * VROW;         // bytes per V tile
-  static constexpr int LDS = 2 * KT + 2 * VT;  // [K0][K1][V0][V1]
+  static constexpr int LDS = 2 * KT + 2 * VT;  // two K and two V buffers
 };
 
 template <int D, bool CAUSAL, class T>
@@ -181,9 +181,10 @@ fwd_kernel(FwdParams p) {
   static_assert(NT % CPR == 0 && BC % RPP == 0, "tile chunks must divide over the workgroup");
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* const kbuf = smem;           // two K tiles
-  uint8_t* const vbuf = smem + 2 * KT;  // two V tiles
+  // Two K and two V tile buffers as separate LDS objects: the loop's buffer parity is a
+  // compile-time value, so the compiler can see that the direct-to-LDS loads of the next
+  // tiles never touch the buffers being read and does not wait for them early.
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds0[KT], k_lds1[KT], v_lds0[VT], v_lds1[VT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -270,11 +271,13 @@ fwd_kernel(FwdParams p) {
       }
     }
   };
+  // `buf` is a literal in the main loop (so buffer addresses are constants) and j & 1 in the
+  // diagonal/tail iterations.
   auto load_k = [&](int tile, int buf) {
-    load_tile(tile, kbase, kbuf + buf * KT, k_vo, IntC<KI>{}, IntC<KSL>{});
+    load_tile(tile, kbase, buf ? k_lds1 : k_lds0, k_vo, IntC<KI>{}, IntC<KSL>{});
   };
   auto load_v = [&](int tile, int buf) {
-    load_tile(tile, vbase, vbuf + buf * VT, v_vo, IntC<VI>{}, IntC<VSL>{});
+    load_tile(tile, vbase, buf ? v_lds1 : v_lds0, v_vo, IntC<VI>{}, IntC<VSL>{});
   };
 
   // ---- per-lane LDS read bases
@@ -288,7 +291,7 @@ fwd_kernel(FwdParams p) {
   const int v_rd = (4 * (grp >> 1) + (gi >> 2)) * VROW + (2 * (grp & 1) + ((gi & 3) >> 1)) * 16 + (gi & 1) * 8;
 
   auto gemm1 = [&](int buf, f32x16 (&s)[MT1]) {
-    const uint8_t* kl = kbuf + buf * KT + k_rd;
+    const uint8_t* kl = (buf ? k_lds1 : k_lds0) + k_rd;
 #pragma unroll
     for (int mt = 0; mt < MT1; ++mt) {
       s[mt] = f32x16{};
@@ -301,7 +304,7 @@ fwd_kernel(FwdParams p) {
   };
 
   auto gemm2 = [&](int buf, const x8 (&pf)[KS2], const x8* pl) {
-    const uint8_t* vl = vbuf + buf * VT + v_rd;
+    const uint8_t* vl = (buf ? v_lds1 : v_lds0) + v_rd;
 #pragma unroll
     for (int md = 0; md < MT2; ++md)
 #pragma unroll
@@ -393,49 +396,101 @@ fwd_kernel(FwdParams p) {
   if (ntiles > 1) load_k(1, 1);
   __syncthreads();  // waits for the loads (vmcnt) before the barrier
 
-  f32x16 s_cur[MT1];
-  gemm1(0, s_cur);
+  f32x16 s_a[MT1], s_b[MT1];
+  gemm1(0, s_a);
   __syncthreads();  // every wave has read K(0) before iteration 0 reloads its buffer
 
   // ---- tile loop. Iteration j: loads of K(j+2), V(j+1) in flight; softmax(j) with the
-  //      MFMAs of GEMM1(j+1); GEMM2(j); the staged loads go to LDS; barrier.
+  //      MFMAs of GEMM1(j+1); GEMM2(j); barrier. Scores of tile j are in `sc`, those of
+  //      tile j+1 go to `sn`.
   //      Tiles below `nfull` are visible to every query of the workgroup and inside Nk, so
   //      their iterations carry no masking code; the rest (diagonal and tail tiles) mask,
   //      and a wave whose queries all precede a tile skips that tile's math.
   int nfull = Nk / BC;
   if (CAUSAL) nfull = min(nfull, (q_wg0 + 1) / BC);
-  auto iteration = [&](const int j, auto split_tag, auto mask_tag) {
-    constexpr bool SPLIT = decltype(split_tag)::value;
-    constexpr bool MASKED = decltype(mask_tag)::value;
-    const bool more_k = j + 2 < ntiles, more_v = j + 1 < ntiles;
-    if (more_k) load_k(j + 2, j & 1);
-    if (more_v) load_v(j + 1, (j + 1) & 1);
-    const bool active = !MASKED || j < wtiles;
-    const bool next_active = MASKED ? (j + 1 < wtiles) : (j + 1 < ntiles);
-    f32x16 s_next[MT1];
-    if (active) {
-      if (MASKED) mask(j, s_cur);
-      max_rescale(s_cur);
-      x8 pf[KS2];
-      x8 pl[SPLIT ? KS2 : 1];
-      if (next_active) gemm1((j + 1) & 1, s_next);
-      softmax(s_cur, pf, SPLIT ? pl : nullptr);
-      gemm2(j & 1, pf, SPLIT ? pl : nullptr);
-    }
-    __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
-    if (next_active) {
+  // main iterations: unmasked and followed by a next tile, so the body has no branch
+  // between the rescale decision and the barrier and is scheduled as one region
+  const int nmain = min(nfull, ntiles - 1);
+
+  // Instruction interleave of the main body (one scheduling region). Phase 1: the MFMAs of
+  // GEMM1(j+1) alternate with the softmax VALU work of tile j (about 4 VALU ops per score
+  // element: fma, exp, fp32 add, half a pack, half a dot2); LDS reads run PF fragments
+  // ahead of the MFMA that consumes them, and the last slots start on the V fragments of
+  // GEMM2. Phase 2: the MFMAs of GEMM2(j), PF V fragments ahead.
+  constexpr int PF = 4;
+  constexpr int N1 = MT1 * KS1, N2 = MT2 * KS2;
+  constexpr int VPM = (4 * (BC / 2) + N1 - 1) / N1;
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // K fragments 0..PF-1
 #pragma unroll
-      for (int mt = 0; mt < MT1; ++mt) s_cur[mt] = s_next[mt];
+    for (int i = 0; i < N1; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+      if (i + PF < N1)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next K read
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // first V reads
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);             // VALU
+    }
+#pragma unroll
+    for (int i = 0; i < N2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i + PF < N2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
     }
   };
 
-  if (nfull > 0)
-    iteration(0, BoolC<true>{}, BoolC<false>{});
-  else
-    iteration(0, BoolC<true>{}, BoolC<true>{});
-  int j = 1;
-  for (; j < nfull; ++j) iteration(j, BoolC<false>{}, BoolC<false>{});
-  for (; j < ntiles; ++j) iteration(j, BoolC<false>{}, BoolC<true>{});
+  auto iteration = [&](const int j, f32x16 (&sc)[MT1], f32x16 (&sn)[MT1], auto split_tag,
+                       auto mask_tag, auto par_tag) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    constexpr bool MASKED = decltype(mask_tag)::value;
+    // j & 1: a literal in the main loop, computed in the diagonal/tail iterations
+    const int par = decltype(par_tag)::value >= 0 ? decltype(par_tag)::value : (j & 1);
+    const bool more_k = j + 2 < ntiles, more_v = j + 1 < ntiles;
+    if (more_k) load_k(j + 2, par);
+    if (more_v) load_v(j + 1, 1 - par);
+    const bool active = !MASKED || j < wtiles;
+    const bool next_active = MASKED ? (j + 1 < wtiles) : true;
+    if (active) {
+      if (MASKED) mask(j, sc);
+      max_rescale(sc);
+      x8 pf[KS2];
+      x8 pl[SPLIT ? KS2 : 1];
+      if (next_active) gemm1(1 - par, sn);
+      softmax(sc, pf, SPLIT ? pl : nullptr);
+      gemm2(par, pf, SPLIT ? pl : nullptr);
+      if (!MASKED && !SPLIT) interleave();
+    }
+    __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
+  };
+
+  using T0 = BoolC<false>;
+  using T1 = BoolC<true>;
+  int j = 0;
+  if (nmain > 0) {
+    iteration(0, s_a, s_b, T1{}, T0{}, IntC<0>{});
+    j = 1;
+    for (; j + 1 < nmain; j += 2) {
+      iteration(j, s_b, s_a, T0{}, T0{}, IntC<1>{});
+      iteration(j + 1, s_a, s_b, T0{}, T0{}, IntC<0>{});
+    }
+    if (j < nmain) {
+      iteration(j, s_b, s_a, T0{}, T0{}, IntC<1>{});
+      ++j;
+    }
+  } else {
+    iteration(0, s_a, s_b, T1{}, T1{}, IntC<0>{});
+    j = 1;
+  }
+  // diagonal and tail tiles; scores of tile j move to s_a first
+  if (j < ntiles && (j & 1)) {
+#pragma unroll
+    for (int mt = 0; mt < MT1; ++mt) s_a[mt] = s_b[mt];
+  }
+  for (; j < ntiles; ++j) {
+    iteration(j, s_a, s_b, T0{}, T1{}, IntC<-1>{});
+#pragma unroll
+    for (int mt = 0; mt < MT1; ++mt) s_a[mt] = s_b[mt];
+  }
 
   // ---- epilogue: combine the two lane halves' sums, normalise, store O and LSE
   lL += other_half(lL);
