@@ -290,25 +290,42 @@ fwd_kernel(FwdParams p) {
   const int grp = lane >> 4, gi = lane & 15;
   const int v_rd = (4 * (grp >> 1) + (gi >> 2)) * VROW + (2 * (grp & 1) + ((gi & 3) >> 1)) * 16 + (gi & 1) * 8;
 
+  // Back-to-back MFMAs that accumulate into the same registers issue at roughly half rate,
+  // so both products alternate between independent accumulators: GEMM1 between its score
+  // tiles (or, with a single score tile, between even and odd k-steps summed at the end),
+  // GEMM2 between its output tiles.
   auto gemm1 = [&](int buf, f32x16 (&s)[MT1]) {
     const uint8_t* kl = (buf ? k_lds1 : k_lds0) + k_rd;
+    if constexpr (MT1 >= 2) {
 #pragma unroll
-    for (int mt = 0; mt < MT1; ++mt) {
-      s[mt] = f32x16{};
+      for (int mt = 0; mt < MT1; ++mt) s[mt] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < KS1; ++t) {
-        u32x4 raw = *(const u32x4*)(kl + mt * 32 * KROW + t * 32);
-        s[mt] = T::mfma(__builtin_bit_cast(x8, raw), qf[t], s[mt]);
+      for (int t = 0; t < KS1; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT1; ++mt) {
+          u32x4 raw = *(const u32x4*)(kl + mt * 32 * KROW + t * 32);
+          s[mt] = T::mfma(__builtin_bit_cast(x8, raw), qf[t], s[mt]);
+        }
+    } else {
+      f32x16 s_odd = f32x16{};
+      s[0] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KS1; t += 2) {
+        u32x4 r0 = *(const u32x4*)(kl + t * 32);
+        u32x4 r1 = *(const u32x4*)(kl + (t + 1) * 32);
+        s[0] = T::mfma(__builtin_bit_cast(x8, r0), qf[t], s[0]);
+        s_odd = T::mfma(__builtin_bit_cast(x8, r1), qf[t + 1], s_odd);
       }
+      s[0] += s_odd;
     }
   };
 
   auto gemm2 = [&](int buf, const x8 (&pf)[KS2], const x8* pl) {
     const uint8_t* vl = (buf ? v_lds1 : v_lds0) + v_rd;
 #pragma unroll
-    for (int md = 0; md < MT2; ++md)
+    for (int u = 0; u < KS2; ++u)
 #pragma unroll
-      for (int u = 0; u < KS2; ++u) {
+      for (int md = 0; md < MT2; ++md) {
         const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(vl + (16 * u) * VROW + md * 64));
         const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
