@@ -17,9 +17,10 @@
 //     scalar, and P^T feeds the second MFMA's B operand straight from registers;
 //   * V^T is read with ds_read_b64_tr_b16 (LDS transpose read), so V stays in its natural
 //     [key][d] layout in LDS;
-//   * K/V tiles are double-buffered in LDS; rows are padded (K by 16 B, V by 32 B) so that
-//     the 16-byte K reads of 16 consecutive rows and the 4-row transpose reads of V hit
-//     distinct banks, and every LDS read address is one per-lane base plus an immediate;
+//   * K/V tiles are double-buffered in LDS; rows are padded (K by 16 B, V by 64 B) so that
+//     the 16-byte K reads of 16 consecutive rows and the transpose reads of V (two 16-lane
+//     groups, 4 rows x 32 B each) hit distinct banks, and every LDS read address is one
+//     per-lane base plus an immediate;
 //   * software pipeline inside each wave: while the softmax of tile j runs on the VALU,
 //     the score MFMAs of tile j+1 are in flight; then the P.V MFMAs of tile j. K(j+2) and
 //     V(j+1) are loaded at the top of iteration j by buffer loads that write LDS directly
@@ -156,7 +157,7 @@ struct Layout {
   static constexpr int NW = TileCfg<D>::NW, BC = TileCfg<D>::BC;
   static constexpr int BR = NW * 32;           // query rows per workgroup
   static constexpr int KROW = D * 2 + 16;      // padded LDS row pitch of K (bytes)
-  static constexpr int VROW = D * 2 + 32;      // padded LDS row pitch of V (bytes)
+  static constexpr int VROW = D * 2 + 64;      // padded LDS row pitch of V (bytes)
   static constexpr int KT = BC * KROW;         // bytes per K tile
   static constexpr int VT = BC * VROW;         // bytes per V tile
   static constexpr int LDS = 2 * KT + 2 * VT;  // two K and two V buffers
@@ -358,15 +359,19 @@ fwd_kernel(FwdParams p) {
     }
   };
 
-  // Row max of a tile and the lazy rescale of O and the sums (decided per wave).
-  auto max_rescale = [&](f32x16 (&s)[MT1]) {
+  // Row max of a tile in log2 units (c >= 0, so max(s)*c == max(s*c)), over both lane halves.
+  auto rowmax = [&](const f32x16 (&s)[MT1]) -> float {
     float mx = s[0][0];
 #pragma unroll
     for (int mt = 0; mt < MT1; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[mt][r]);
     mx = __builtin_fmaxf(mx, other_half(mx));
-    const float mtile = mx * c;  // c >= 0, so max(s)*c == max(s*c)
+    return mx * c;
+  };
+  // Lazy rescale of O and the sums, decided per wave: only when some row's tile max exceeds
+  // its running max by more than TAU.
+  auto rescale_to = [&](const float mtile) {
     const bool grow = mtile > m_run + TAU;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float mnew = __builtin_fmaxf(m_run, mtile);
@@ -425,58 +430,122 @@ fwd_kernel(FwdParams p) {
   //      and a wave whose queries all precede a tile skips that tile's math.
   int nfull = Nk / BC;
   if (CAUSAL) nfull = min(nfull, (q_wg0 + 1) / BC);
-  // main iterations: unmasked and followed by a next tile, so the body has no branch
-  // between the rescale decision and the barrier and is scheduled as one region
+  // main iterations: unmasked and followed by a next tile
   const int nmain = min(nfull, ntiles - 1);
 
-  // Instruction interleave of the main body (one scheduling region). Phase 1: the MFMAs of
-  // GEMM1(j+1) alternate with the softmax VALU work of tile j (about 4 VALU ops per score
-  // element: fma, exp, fp32 add, half a pack, half a dot2); LDS reads run PF fragments
-  // ahead of the MFMA that consumes them, and the last slots start on the V fragments of
-  // GEMM2. Phase 2: the MFMAs of GEMM2(j), PF V fragments ahead.
-  constexpr int PF = 4;
-  constexpr int N1 = MT1 * KS1, N2 = MT2 * KS2;
-  constexpr int VPM = (4 * (BC / 2) + N1 - 1) / N1;
-  auto interleave = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // K fragments 0..PF-1
-#pragma unroll
-    for (int i = 0; i < N1; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
-      if (i + PF < N1)
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next K read
-      else
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // first V reads
-      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);             // VALU
-    }
-#pragma unroll
-    for (int i = 0; i < N2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      if (i + PF < N2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
-    }
-  };
+  // Scaled row max of the scores of the next tile, computed at the end of each iteration
+  // for the main iterations (whose tiles need no mask).
+  float mt_cur = 0.f;
 
+  // Generic iteration (first tile, diagonal and tail tiles): straightforward order.
   auto iteration = [&](const int j, f32x16 (&sc)[MT1], f32x16 (&sn)[MT1], auto split_tag,
-                       auto mask_tag, auto par_tag) {
+                       auto mask_tag) {
     constexpr bool SPLIT = decltype(split_tag)::value;
     constexpr bool MASKED = decltype(mask_tag)::value;
-    // j & 1: a literal in the main loop, computed in the diagonal/tail iterations
-    const int par = decltype(par_tag)::value >= 0 ? decltype(par_tag)::value : (j & 1);
+    const int par = j & 1;
     const bool more_k = j + 2 < ntiles, more_v = j + 1 < ntiles;
     if (more_k) load_k(j + 2, par);
     if (more_v) load_v(j + 1, 1 - par);
     const bool active = !MASKED || j < wtiles;
-    const bool next_active = MASKED ? (j + 1 < wtiles) : true;
+    const bool next_active = MASKED ? (j + 1 < wtiles) : more_v;
     if (active) {
       if (MASKED) mask(j, sc);
-      max_rescale(sc);
+      rescale_to(rowmax(sc));
       x8 pf[KS2];
       x8 pl[SPLIT ? KS2 : 1];
       if (next_active) gemm1(1 - par, sn);
       softmax(sc, pf, SPLIT ? pl : nullptr);
       gemm2(par, pf, SPLIT ? pl : nullptr);
-      if (!MASKED && !SPLIT) interleave();
+      if (next_active) mt_cur = rowmax(sn);
     }
+    __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
+  };
+
+  // Main iteration (unmasked tile j, tile j+1 exists), with an explicit instruction order:
+  //   phase 1: each GEMM1(j+1) MFMA is issued with the LDS read PF steps ahead and with one
+  //            slice of the softmax VALU work of tile j (fma, exp, sums, pack of a pair);
+  //            the last steps start reading the V fragments of GEMM2;
+  //   phase 2: each GEMM2(j) MFMA with the V read PF steps ahead and with one slice of the
+  //            row max of tile j+1 (which the next iteration's rescale decision needs).
+  // sched_barrier fences keep each step's instructions together.
+  constexpr int PF = 4;
+  constexpr int N1 = MT1 * KS1, N2 = MT2 * KS2;
+  constexpr int NPAIR = 8 * MT1;  // score pairs per lane per tile
+  auto main_iteration = [&](const int j, f32x16 (&sc)[MT1], f32x16 (&sn)[MT1], auto par_tag) {
+    constexpr int PAR = decltype(par_tag)::value;  // j & 1
+    if (j + 2 < ntiles) load_k(j + 2, PAR);
+    load_v(j + 1, 1 - PAR);
+    rescale_to(mt_cur);
+    const float negm = -m_run;
+    const uint8_t* kl = (PAR ? k_lds0 : k_lds1) + k_rd;  // K(j+1): buffer 1 - PAR
+    const uint8_t* vl = (PAR ? v_lds1 : v_lds0) + v_rd;  // V(j): buffer PAR
+    auto kfrag = [&](const int i) -> x8 {
+      const int t = MT1 >= 2 ? i / MT1 : i, mt = MT1 >= 2 ? i % MT1 : 0;
+      return __builtin_bit_cast(x8, *(const u32x4*)(kl + mt * 32 * KROW + t * 32));
+    };
+    auto vfrag = [&](const int i) -> x8 {
+      const int u = i / MT2, md = i % MT2;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * u) * VROW + md * 64));
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * u + 8) * VROW + md * 64));
+      u32x4 raw;
+      raw[0] = __builtin_bit_cast(u32x2, lo4)[0];
+      raw[1] = __builtin_bit_cast(u32x2, lo4)[1];
+      raw[2] = __builtin_bit_cast(u32x2, hi4)[0];
+      raw[3] = __builtin_bit_cast(u32x2, hi4)[1];
+      return __builtin_bit_cast(x8, raw);
+    };
+    x8 kf[N1], vf[N2], pf[KS2];
+    f32x16 s_odd;
+    float sumL0 = 0.f, sumL1 = 0.f, sumO = 0.f;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N1; ++i) {
+      if (i + PF < N1)
+        kf[i + PF] = kfrag(i + PF);
+      else
+        vf[i + PF - N1] = vfrag(i + PF - N1);
+      if constexpr (MT1 >= 2) {
+        const int t = i / MT1, mt = i % MT1;
+        sn[mt] = T::mfma(kf[i], qf[t], t == 0 ? f32x16{} : sn[mt]);
+      } else if (i & 1) {
+        s_odd = T::mfma(kf[i], qf[i], i == 1 ? f32x16{} : s_odd);
+      } else {
+        sn[0] = T::mfma(kf[i], qf[i], i == 0 ? f32x16{} : sn[0]);
+      }
+      if ((i * NPAIR) % N1 == 0) {
+        const int pi = i * NPAIR / N1, mt = pi / 8, r = (pi % 8) * 2;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][r], c, negm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][r + 1], c, negm));
+        sumL0 += p0;
+        sumL1 += p1;
+        const x2 pb = T::cvt2(p0, p1);
+        sumO = T::dot2(pb, one2, sumO);
+        const int u = mt * 2 + (r >> 3);
+        pf[u][(r & 7)] = pb[0];
+        pf[u][(r & 7) + 1] = pb[1];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lL += sumL0 + sumL1;
+    lO += sumO;
+    float mx = -__builtin_inff();
+    constexpr int VPS = (16 * MT1) / N2;  // next-tile scores folded into the max per step
+#pragma unroll
+    for (int i = 0; i < N2; ++i) {
+      if (i + PF < N2) vf[i + PF] = vfrag(i + PF);
+      const int u = i / MT2, md = i % MT2;
+      acc[md] = T::mfma(vf[i], pf[u], acc[md]);
+#pragma unroll
+      for (int e = i * VPS; e < (i + 1) * VPS; ++e) {
+        if constexpr (MT1 == 1) sn[0][e] += s_odd[e];
+        mx = __builtin_fmaxf(mx, sn[e / 16][e % 16]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mx = __builtin_fmaxf(mx, other_half(mx));
+    mt_cur = mx * c;
     __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
   };
 
@@ -484,18 +553,18 @@ fwd_kernel(FwdParams p) {
   using T1 = BoolC<true>;
   int j = 0;
   if (nmain > 0) {
-    iteration(0, s_a, s_b, T1{}, T0{}, IntC<0>{});
+    iteration(0, s_a, s_b, T1{}, T0{});
     j = 1;
     for (; j + 1 < nmain; j += 2) {
-      iteration(j, s_b, s_a, T0{}, T0{}, IntC<1>{});
-      iteration(j + 1, s_a, s_b, T0{}, T0{}, IntC<0>{});
+      main_iteration(j, s_b, s_a, IntC<1>{});
+      main_iteration(j + 1, s_a, s_b, IntC<0>{});
     }
     if (j < nmain) {
-      iteration(j, s_b, s_a, T0{}, T0{}, IntC<1>{});
+      main_iteration(j, s_b, s_a, IntC<1>{});
       ++j;
     }
   } else {
-    iteration(0, s_a, s_b, T1{}, T1{}, IntC<0>{});
+    iteration(0, s_a, s_b, T1{}, T1{});
     j = 1;
   }
   // diagonal and tail tiles; scores of tile j move to s_a first
@@ -504,7 +573,7 @@ fwd_kernel(FwdParams p) {
     for (int mt = 0; mt < MT1; ++mt) s_a[mt] = s_b[mt];
   }
   for (; j < ntiles; ++j) {
-    iteration(j, s_a, s_b, T0{}, T1{}, IntC<-1>{});
+    iteration(j, s_a, s_b, T0{}, T1{});
 #pragma unroll
     for (int mt = 0; mt < MT1; ++mt) s_a[mt] = s_b[mt];
   }
