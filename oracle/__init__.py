@@ -4,6 +4,6 @@ Test infrastructure only: imported by tests/, the smoke check and the benchmark'
 CPU-baseline leg, never by the library or its Python binding.
 """
 
-from .attention import attention_bruteforce, attention_ref, kv_head_of
+from .attention import attention_bruteforce, attention_bwd_ref, attention_ref, kv_head_of
 
-__all__ = ["attention_ref", "attention_bruteforce", "kv_head_of"]
+__all__ = ["attention_ref", "attention_bruteforce", "attention_bwd_ref", "kv_head_of"]

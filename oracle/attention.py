@@ -36,9 +36,16 @@ Readings where the pages are silent (each is listed in the design notes):
   * LSE is the natural-log log-sum-exp of the *scaled* scores over visible keys,
     laid out [B, Hq, Nq].
 
+The backward pass (attention_bwd_ref) is the gradient of sum(O * dO) with respect to
+q, k and v, written out from the same definition (the pages list a backward pass next to
+the forward: "[RFC] FA4 - head_dim=256 & head_dim=512", Phase 1 and the backward tables
+of "Performance Snapshot").
+
 Pins: tests/test_oracle.py checks this module against hand-worked cases, closed
 forms, invariants, a brute-force per-row formulation with math.fsum and torch's
-own CPU scaled_dot_product_attention in float64. Nothing here is "parity unpinned".
+own CPU scaled_dot_product_attention in float64; tests/test_oracle_bwd.py checks the
+backward against torch autograd in float64, central finite differences and closed forms.
+Nothing here is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -47,7 +54,7 @@ import math
 
 import numpy as np
 
-__all__ = ["attention_ref", "attention_bruteforce", "kv_head_of"]
+__all__ = ["attention_ref", "attention_bruteforce", "attention_bwd_ref", "kv_head_of"]
 
 
 def kv_head_of(h: int, hq: int, hkv: int) -> int:
@@ -166,3 +173,48 @@ def attention_bruteforce(q, k, v, causal: bool, scale: float):
                     O[b, i, h, t] = math.fsum(w[j] * v[b, j, kvh, t] for j in s) / den
                 LSE[b, h, i] = mx + math.log(den)
     return O, LSE
+
+
+def attention_bwd_ref(q, k, v, dout, causal: bool, scale: float):
+    """Exact attention backward in float64: gradients of sum(O * dout) w.r.t. q, k and v.
+
+    With S = scale * Q K^T (causal: -inf above the diagonal), P = softmax(S) per row,
+    O = P V:
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - D),  D_i = sum_j P_ij dP_ij  (= sum_d dO_id O_id)
+        dQ = scale * dS K
+        dK = scale * dS^T Q
+    For grouped-query heads, dK and dV of a KV head sum the contributions of every query
+    head of its group. Layouts as in attention_ref: q/dout/dq [B, Nq, Hq, d], k/v/dk/dv
+    [B, Nk, Hkv, d]. Returns (dq, dk, dv) as float64 numpy arrays.
+    """
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if causal and Nq != Nk:
+        raise ValueError("causal attention is defined here for Nq == Nk only")
+    scale = float(scale)
+    dq = np.zeros((B, Nq, Hq, d))
+    dk = np.zeros((B, Nk, Hkv, d))
+    dv = np.zeros((B, Nk, Hkv, d))
+    all_rows = slice(None)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = kv_head_of(h, Hq, Hkv)
+            Qh = _slice_f64(q, b, all_rows, h)
+            Kh = _slice_f64(k, b, all_rows, kvh)
+            Vh = _slice_f64(v, b, all_rows, kvh)
+            dOh = _slice_f64(dout, b, all_rows, h)
+            S = scale * (Qh @ Kh.T)
+            if causal:
+                S[np.arange(Nk)[None, :] > np.arange(Nq)[:, None]] = -np.inf
+            m = S.max(axis=1, keepdims=True)
+            P = np.exp(S - m)
+            P /= P.sum(axis=1, keepdims=True)
+            dv[b, :, kvh, :] += P.T @ dOh
+            dP = dOh @ Vh.T
+            D = (P * dP).sum(axis=1, keepdims=True)
+            dS = P * (dP - D)
+            dq[b, :, h, :] = scale * (dS @ Kh)
+            dk[b, :, kvh, :] += scale * (dS.T @ Qh)
+    return dq, dk, dv
