@@ -1,6 +1,7 @@
 """MI355X (gfx950) exact-attention forward pass: Python binding of libfa.so.
 
     o, lse = forward(q, k, v, causal=False, scale=None)
+    dq, dk, dv = backward(q, k, v, o, lse, dout, causal=False, scale=None)
 
 q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] (bf16 or fp16, contiguous, on the GPU);
 returns o [B, Nq, Hq, d] (same dtype) and lse [B, Hq, Nq] (fp32). torch provides device
@@ -15,7 +16,7 @@ import math
 
 from . import _lib
 
-__all__ = ["forward", "check_args", "FaError"]
+__all__ = ["forward", "backward", "check_args", "FaError"]
 
 
 class FaError(ValueError):
@@ -81,3 +82,54 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if rc != 0:
         _raise(rc)
     return out, lse
+
+
+def _check_tensor(name, t, torch):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None):
+    """Gradients (dq, dk, dv) of sum(o * dout) for o, lse = forward(q, k, v, causal, scale)."""
+    import torch
+
+    lib = _lib.load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
+        _check_tensor(name, t, torch)
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise ValueError("q, k, v, o and dout must share one dtype")
+    if q.dtype == torch.bfloat16:
+        fn = lib.fa_bwd
+    elif q.dtype == torch.float16:
+        fn = lib.fa_bwd_f16
+    else:
+        raise ValueError("dtype must be bfloat16 or float16")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [batch, seq, heads, head_dim]")
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk_ = k.shape
+    if Bk != B or dk_ != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q/k/v shapes do not match: q [B,Nq,Hq,d], k and v [B,Nk,Hkv,d]")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have the shape of q")
+    if tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    nbytes = int(lib.fa_bwd_workspace_bytes(B, Nq, Hq))
+    ws = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes, B, Nq, Nk, Hq, Hkv, d,
+                int(bool(causal)), float(scale), stream)
+    if rc != 0:
+        _raise(rc)
+    return dq, dk, dv

@@ -23,6 +23,7 @@ FA_ERR_SCALE = -5
 FA_ERR_ALIGN = -6
 FA_ERR_TOO_LARGE = -7
 FA_ERR_LAUNCH = -8
+FA_ERR_WORKSPACE = -9
 
 _lib = None
 
@@ -30,6 +31,8 @@ _I = ctypes.c_int
 _P = ctypes.c_void_p
 _FWD_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 _CHECK_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float]
+_BWD_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _I, _I, _I,
+             ctypes.c_float, _P]
 
 
 def load():
@@ -43,6 +46,12 @@ def load():
             fn = getattr(lib, name)
             fn.argtypes = _FWD_ARGS
             fn.restype = _I
+        for name in ("fa_bwd", "fa_bwd_f16"):
+            fn = getattr(lib, name)
+            fn.argtypes = _BWD_ARGS
+            fn.restype = _I
+        lib.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I]
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_check.argtypes = _CHECK_ARGS
         lib.fa_fwd_check.restype = _I
         lib.fa_strerror.argtypes = [_I]

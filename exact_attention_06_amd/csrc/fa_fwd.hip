@@ -9,6 +9,7 @@
 
 #include "fa_fwd.h"
 #include "fa_kernel.h"
+#include "fa_bwd_kernel.h"
 
 namespace {
 
@@ -65,6 +66,63 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   return causal ? launch<256, true, T>(prm, grid, s) : launch<256, false, T>(prm, grid, s);
 }
 
+size_t bwd_ws_bytes(int B, int Nq, int Hq) {
+  if (B <= 0 || Nq <= 0 || Hq <= 0) return 0;
+  return (size_t)B * Hq * Nq * sizeof(float);
+}
+
+template <int D, bool CAUSAL, class T>
+int launch_bwd(const fa::BwdParams& base, hipStream_t stream) {
+  constexpr int NW = fa::BwdCfg<D>::NW, BR = NW * 32;
+  fa::BwdParams prm = base;
+  prm.ntile = (prm.Nq + BR - 1) / BR;
+  hipLaunchKernelGGL((fa::bwd_dq_kernel<D, CAUSAL, T>), dim3(prm.B * prm.Hq * prm.ntile), dim3(NW * 64), 0,
+                     stream, prm);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  prm.ntile = (prm.Nk + BR - 1) / BR;
+  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<D, CAUSAL, T>), dim3(prm.B * prm.Hkv * prm.ntile), dim3(NW * 64), 0,
+                     stream, prm);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <class T>
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+            void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, int B, int Nq, int Nk, int Hq, int Hkv,
+            int d, int causal, float scale, void* stream) {
+  int st = check(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale);
+  if (st != FA_OK) return st;
+  if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (((uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15) return FA_ERR_ALIGN;
+  if (!ws || ws_bytes < bwd_ws_bytes(B, Nq, Hq) || ((uintptr_t)ws & 3)) return FA_ERR_WORKSPACE;
+  const int64_t BR = fa::BwdCfg<128>::NW * 32;
+  if ((int64_t)B * Hq * ((Nq + BR - 1) / BR) > INT_MAX || (int64_t)B * Hkv * ((Nk + BR - 1) / BR) > INT_MAX)
+    return FA_ERR_TOO_LARGE;
+  fa::BwdParams prm;
+  prm.q = (const uint8_t*)q;
+  prm.k = (const uint8_t*)k;
+  prm.v = (const uint8_t*)v;
+  prm.o = (const uint8_t*)o;
+  prm.lse = lse;
+  prm.dout = (const uint8_t*)dout;
+  prm.dq = (uint8_t*)dq;
+  prm.dk = (uint8_t*)dk;
+  prm.dv = (uint8_t*)dv;
+  prm.dsum = (float*)ws;
+  prm.B = B;
+  prm.Nq = Nq;
+  prm.Nk = Nk;
+  prm.Hq = Hq;
+  prm.Hkv = Hkv;
+  prm.group = Hq / Hkv;
+  prm.ntile = 0;
+  prm.c = scale * fa::LOG2E;
+  prm.scale = scale;
+  hipStream_t s = (hipStream_t)stream;
+  if (d == 128)
+    return causal ? launch_bwd<128, true, T>(prm, s) : launch_bwd<128, false, T>(prm, s);
+  return causal ? launch_bwd<256, true, T>(prm, s) : launch_bwd<256, false, T>(prm, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +142,22 @@ int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
   return run<fa::F16>(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale, stream);
 }
 
+size_t fa_bwd_workspace_bytes(int B, int Nq, int Hq) { return bwd_ws_bytes(B, Nq, Hq); }
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Nq, int Nk,
+           int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  return run_bwd<fa::Bf16>(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Nq, Nk, Hq, Hkv, d,
+                           causal, scale, stream);
+}
+
+int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Nq, int Nk,
+               int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  return run_bwd<fa::F16>(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Nq, Nk, Hq, Hkv, d,
+                          causal, scale, stream);
+}
+
 const char* fa_strerror(int code) {
   switch (code) {
     case FA_OK: return "ok";
@@ -95,6 +169,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_TOO_LARGE: return "problem too large for 32-bit grid or sequence indexing";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
+    case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or smaller than fa_bwd_workspace_bytes";
     default: return "unknown fa status code";
   }
 }

@@ -40,6 +40,8 @@
 #ifndef FA_FWD_H
 #define FA_FWD_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -54,7 +56,9 @@ enum fa_status {
   FA_ERR_SCALE = -5,        /* scale is NaN, infinite or negative                          */
   FA_ERR_ALIGN = -6,        /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_TOO_LARGE = -7,    /* the work grid or a per-head extent exceeds 2^31 - 1         */
-  FA_ERR_LAUNCH = -8        /* the HIP launch reported an error                            */
+  FA_ERR_LAUNCH = -8,       /* the HIP launch reported an error                            */
+  FA_ERR_WORKSPACE = -9     /* backward: workspace NULL or smaller than
+                               fa_bwd_workspace_bytes(B, Nq, Hq)                           */
 };
 
 /* Forward pass, bf16 q/k/v/o, fp32 LSE. Arguments as described above; `scale` multiplies
@@ -76,6 +80,35 @@ const char* fa_strerror(int code);
  * launch would proceed). Makes no HIP call. */
 int fa_fwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale);
+
+/*
+ * Backward pass: gradients of sum(O * dout) with respect to q, k and v, for the forward
+ * above ("[RFC] FA4 - head_dim=256 & head_dim=512", Phase 1 "Backward kernel").
+ *
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D) with D_i = sum_d dO_id O_id,
+ *   dQ = scale * dS K,  dK = scale * dS^T Q,  P = exp(scale * Q K^T - LSE) (causal-masked).
+ * For grouped-query heads dK/dV of a KV head sum over its query heads.
+ *
+ * Inputs: q, k, v as for fa_fwd; o and lse as produced by fa_fwd with the same arguments;
+ * dout [B, Nq, Hq, d] (same element type). Outputs: dq [B, Nq, Hq, d], dk and dv
+ * [B, Nk, Hkv, d] (element type of the inputs; fully overwritten). workspace: caller-owned
+ * device memory of at least fa_bwd_workspace_bytes(B, Nq, Hq) bytes, 4-byte aligned; it
+ * receives D (fp32 [B, Hq, Nq]) and holds no state between calls. Same execution and error
+ * rules as fa_fwd (FA_ERR_WORKSPACE for a missing or short workspace); two kernels run in
+ * order on `stream`.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Nq, int Hq);
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal,
+           float scale, void* stream);
+
+/* Same as fa_bwd with fp16 tensors. */
+int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int Nq, int Nk, int Hq, int Hkv, int d,
+               int causal, float scale, void* stream);
 
 #ifdef __cplusplus
 }

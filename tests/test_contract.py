@@ -33,7 +33,8 @@ def _fwd(fn, **kw):
 def test_library_exports_every_header_symbol():
     lib = _lib.load()
     names = _lib.header_symbols()
-    assert set(names) == {"fa_fwd", "fa_fwd_f16", "fa_strerror", "fa_fwd_check"}
+    assert set(names) == {"fa_fwd", "fa_fwd_f16", "fa_strerror", "fa_fwd_check", "fa_bwd", "fa_bwd_f16",
+                          "fa_bwd_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -99,11 +100,11 @@ def test_entry_points_reject_before_any_hip_call(entry):
 
 def test_strerror_covers_codes():
     seen = set()
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         msg = _lib.strerror(code)
         assert msg and msg != "unknown fa status code"
         seen.add(msg)
-    assert len(seen) == 9
+    assert len(seen) == 10
     assert _lib.strerror(-99) == "unknown fa status code"
 
 
@@ -116,3 +117,32 @@ def test_python_layer_rejects_cpu_tensors():
 def test_python_layer_error_type():
     err = fa.FaError(_lib.FA_ERR_HEADDIM, _lib.strerror(_lib.FA_ERR_HEADDIM))
     assert isinstance(err, ValueError) and "head dim" in str(err)
+
+
+def _bwd(fn, **kw):
+    a = dict(GOOD, **kw)
+    ws = a.get("ws", A + 0x800)
+    wsb = a.get("wsb", 4 * a["B"] * a["Hq"] * a["Nq"])
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a.get("do", A + 0x500), a.get("dq", A + 0x600),
+              a.get("dk", A + 0x700), a.get("dv", A + 0x780), ws, wsb, a["B"], a["Nq"], a["Nk"], a["Hq"],
+              a["Hkv"], a["d"], a["causal"], ctypes.c_float(a["scale"]), None)
+
+
+def test_bwd_workspace_size():
+    lib = _lib.load()
+    assert lib.fa_bwd_workspace_bytes(2, 300, 8) == 4 * 2 * 300 * 8
+    assert lib.fa_bwd_workspace_bytes(0, 300, 8) == 0
+
+
+@pytest.mark.parametrize("entry", ["fa_bwd", "fa_bwd_f16"])
+def test_bwd_rejects_before_any_hip_call(entry):
+    fn = getattr(_lib.load(), entry)
+    assert _bwd(fn, q=0) == _lib.FA_ERR_NULL
+    assert _bwd(fn, do=0) == _lib.FA_ERR_NULL
+    assert _bwd(fn, dk=0) == _lib.FA_ERR_NULL
+    assert _bwd(fn, d=96) == _lib.FA_ERR_HEADDIM
+    assert _bwd(fn, causal=1, Nk=17) == _lib.FA_ERR_CAUSAL_SHAPE
+    assert _bwd(fn, dq=A + 0x604) == _lib.FA_ERR_ALIGN
+    assert _bwd(fn, ws=0) == _lib.FA_ERR_WORKSPACE
+    assert _bwd(fn, wsb=4 * 2 * 300 * 8 - 4) == _lib.FA_ERR_WORKSPACE
+    assert _bwd(fn, ws=A + 0x802) == _lib.FA_ERR_WORKSPACE

@@ -1,0 +1,96 @@
+"""GPU parity of the backward pass (dq, dk, dv through the C ABI) against the fp64 oracle.
+
+The inputs q, k, v, dout are the same bf16/fp16 values on both sides; the GPU's o and lse
+come from its own forward pass (as in training). P and dS enter the MFMAs rounded to the
+input type, and the gradients are rounded to it on output, so the bound is relative to the
+gradient's own scale: per tensor, max-abs error <= 1e-2 * max|ref| and mean-abs error <=
+5e-3 * mean|ref|. Rounding a value to bf16 alone costs up to 2^-9 (1.95e-3) of it and 2^-10
+on average; measured ratios are 2e-3..5.4e-3 (max) and 1.9e-3..3.8e-3 (mean) for bf16 and
+about ten times smaller for fp16. The measured errors are printed for every case.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_06_amd as fa
+from exact_attention_06_amd import workloads as W
+from oracle import attention_bwd_ref
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL, MEAN_REL = 1e-2, 5e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _run(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, head=None):
+    """head=(b, kvh): compare only that KV head's group (dq of its query heads, its dk, dv)."""
+    q, k, v = W.make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, dtype=dtype)
+    g = torch.Generator().manual_seed(seed + 7)
+    do = torch.randn((B, Nq, Hq, d), generator=g).to(dtype)
+    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    _say(f"[gpu] bwd {name} B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} {dtype}")
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    if head is not None:
+        b, kvh = head
+        gsz = Hq // Hkv
+        hs = slice(kvh * gsz, (kvh + 1) * gsz)
+        rq, rk, rv = attention_bwd_ref(q[b:b + 1, :, hs], k[b:b + 1, :, kvh:kvh + 1], v[b:b + 1, :, kvh:kvh + 1],
+                                       do[b:b + 1, :, hs], causal, scale)
+        dq, dk, dv = dq[b:b + 1, :, hs], dk[b:b + 1, :, kvh:kvh + 1], dv[b:b + 1, :, kvh:kvh + 1]
+    else:
+        rq, rk, rv = attention_bwd_ref(q, k, v, do, causal, scale)
+    for tname, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        got = got.float().cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all(), f"{name}/{tname}: non-finite"
+        err = np.abs(got - ref)
+        mx, mean, rmax, rmean = err.max(), err.mean(), np.abs(ref).max(), np.abs(ref).mean()
+        _say(f"  {name}/{tname}: max err {mx:.3e} (max|ref| {rmax:.3e}, ratio {mx / rmax:.2e}) "
+             f"mean err {mean:.3e} (mean|ref| {rmean:.3e}, ratio {mean / rmean:.2e})")
+        assert mx <= MAX_REL * rmax and mean <= MEAN_REL * rmean, f"{name}/{tname}"
+
+
+CASES = [
+    # name,           B,  Nq,   Nk,  Hq, Hkv,  d, seed
+    ("tiny",          1,  256,  256,  2,  2, 128, 61),
+    ("ragged",        1,  257,  257,  8,  8, 128, 62),
+    ("gqa_tail",      2,  300,  300,  4,  2, 128, 63),
+    ("hd256",         1,  200,  200,  2,  1, 256, 64),
+    ("few",           2,    3,    3,  2,  1, 128, 65),
+    ("mid",           1, 1024, 1024,  4,  4, 128, 66),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_bwd_full(case, causal):
+    name, B, Nq, Nk, Hq, Hkv, d, seed = case
+    _run(name, B, Nq, Nk, Hq, Hkv, d, causal, seed)
+
+
+@pytest.mark.parametrize("case", [("rect_qk", 1, 100, 333, 2, 1, 128, 67), ("rect_kq", 1, 333, 90, 2, 2, 256, 68)],
+                         ids=["rect_qk", "rect_kq"])
+def test_bwd_rectangular(case):
+    name, B, Nq, Nk, Hq, Hkv, d, seed = case
+    _run(name, B, Nq, Nk, Hq, Hkv, d, False, seed)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_fp16(d):
+    _run(f"fp16_d{d}", 1, 300, 300, 2, 1, d, True, 69 + d, dtype=torch.float16)
+
+
+FULL_BWD = [W.by_name(n) for n in ("hd128_N8192_mha", "hd128_N8192_gqa4", "hd256_N8192", "hd256_N32768")]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("w", FULL_BWD, ids=[w.name for w in FULL_BWD])
+def test_bwd_full_size_one_head(w, causal):
+    # full-size launch; the oracle covers KV head 0 of the last batch (and its query heads)
+    _run(w.name, w.B, w.N, w.N, w.Hq, w.Hkv, w.d, causal, w.seed, head=(w.B - 1, 0))
