@@ -149,6 +149,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -214,6 +215,37 @@ def main():
             del qx, kx, vx
             torch.cuda.empty_cache()
 
+    # backward pass (gradients of sum(O * dO)); FLOPs counted as 2.5x the forward's
+    # (five N x N x d products), the usual convention
+    backward = []
+    if not args.no_backward:
+        for name in ("hd128_N8192_mha", "hd256_N8192"):
+            x = W.by_name(name)
+            qx, kx, vx = gpu_inputs(x, torch)
+            g = torch.Generator(device="cuda")
+            g.manual_seed(x.seed + 7)
+            dox = torch.randn(qx.shape, generator=g, device="cuda").to(torch.bfloat16)
+            for c in (False, True):
+                o, lse = fa.forward(qx, kx, vx, causal=c, scale=x.scale)
+                for _ in range(2):
+                    fa.backward(qx, kx, vx, o, lse, dox, causal=c, scale=x.scale)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                n = max(1, args.sweep_steps)
+                e0.record()
+                for _ in range(n):
+                    fa.backward(qx, kx, vx, o, lse, dox, causal=c, scale=x.scale)
+                e1.record()
+                torch.cuda.synchronize()
+                m = e0.elapsed_time(e1) / n
+                t = 2.5 * x.flops(c) / (m * 1e-3) / 1e12
+                backward.append({"workload": x.name, "causal": c, "ms": round(m, 4), "tflops": round(t, 1),
+                                 "frac_peak": round(t / PEAK_BF16_TFLOPS, 4)})
+                log(f"[bwd] {x.name:20s} {'causal' if c else 'noncausal':9s} {m:8.3f} ms {t:7.1f} TFLOPS")
+            del qx, kx, vx, dox, o, lse
+            torch.cuda.empty_cache()
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, causal)
     if cpu:
         log(f"[cpu] oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['sample']})")
@@ -243,6 +275,7 @@ def main():
                      "flops_per_launch": flops},
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "backward": backward,
         "kernel_source_hash": kernel_source_hash(),
     }
     if b200:
