@@ -41,8 +41,9 @@ struct BwdParams {
   int B, Nq, Nk, Hq, Hkv;
   int group;
   int ntile;    // work tiles per (b, head) of the kernel (query tiles or key tiles)
-  float c;      // scale * log2(e)
+  float c;      // scale * log2(e); log2(e) when zero_scores is set
   float scale;
+  int zero_scores;  // scale is zero (or below the normal range): every score is exactly 0
 };
 
 template <int D>
@@ -113,6 +114,10 @@ bwd_dq_kernel(BwdParams p) {
     const x8 of = __builtin_bit_cast(x8, *(const u32x4*)(p.o + qrow + off));
 #pragma unroll
     for (int e = 0; e < 8; ++e) dpart += (float)df[t][e] * (float)of[e];
+  }
+  if (p.zero_scores) {  // zero scale: S = 0 exactly (masked scores stay -inf)
+#pragma unroll
+    for (int t = 0; t < KS1; ++t) qf[t] = x8{};
   }
   const float dsum = dpart + other_half(dpart);
   const size_t lrow = ((size_t)b * p.Hq + hq) * Nq + q_ld;
@@ -244,6 +249,10 @@ bwd_dkdv_kernel(BwdParams p) {
     const int off = (16 * t + 8 * hh) * 2;
     kf[t] = __builtin_bit_cast(x8, *(const u32x4*)(p.k + krow + off));
     vf[t] = __builtin_bit_cast(x8, *(const u32x4*)(p.v + krow + off));
+  }
+  if (p.zero_scores) {  // zero scale: S = 0 exactly (masked scores stay -inf)
+#pragma unroll
+    for (int t = 0; t < KS1; ++t) kf[t] = x8{};
   }
   const float c = p.c;
   f32x16 dk[MT2], dv[MT2];

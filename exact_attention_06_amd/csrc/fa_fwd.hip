@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
@@ -56,7 +57,10 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   prm.Hq = Hq;
   prm.Hkv = Hkv;
   prm.group = Hq / Hkv;
-  prm.c = scale * fa::LOG2E;
+  // A zero (or subnormal) scale makes every visible score exactly 0; the kernel then zeroes
+  // Q and uses c = log2(e), since -inf * 0 would turn masked scores into NaN.
+  prm.zero_scores = !(scale * fa::LOG2E >= FLT_MIN);
+  prm.c = prm.zero_scores ? fa::LOG2E : scale * fa::LOG2E;
   const int BR = d == 128 ? br<128>() : br<256>();
   prm.nqt = (Nq + BR - 1) / BR;
   const int grid = B * Hq * prm.nqt;
@@ -115,7 +119,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   prm.Hkv = Hkv;
   prm.group = Hq / Hkv;
   prm.ntile = 0;
-  prm.c = scale * fa::LOG2E;
+  prm.zero_scores = !(scale * fa::LOG2E >= FLT_MIN);  // as in the forward pass
+  prm.c = prm.zero_scores ? fa::LOG2E : scale * fa::LOG2E;
   prm.scale = scale;
   hipStream_t s = (hipStream_t)stream;
   if (d == 128)

@@ -101,7 +101,8 @@ struct FwdParams {
   int B, Nq, Nk, Hq, Hkv;
   int group;      // Hq / Hkv
   int nqt;        // query tiles per (b, h)
-  float c;        // scale * log2(e)
+  float c;        // scale * log2(e); log2(e) when zero_scores is set
+  int zero_scores;  // scale is zero (or below the normal range): every score is exactly 0
 };
 
 template <bool V> struct BoolC { static constexpr bool value = V; };
@@ -149,8 +150,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base,
 
 // Tile configuration per head dim: waves per workgroup, keys per K/V tile.
 template <int D> struct TileCfg;
-template <> struct TileCfg<128> { static constexpr int NW = 8, BC = 64; };
-template <> struct TileCfg<256> { static constexpr int NW = 4, BC = 32; };
+// SEQ: one score buffer and a plain per-tile order (two workgroups share a CU and overlap
+// each other); otherwise the scores of the next tile are computed during the softmax of the
+// current one (one workgroup per CU, explicit MFMA/VALU interleave). WPE: waves per SIMD
+// the register budget is sized for.
+template <> struct TileCfg<128> { static constexpr int NW = 8, BC = 64, WPE = 2; static constexpr bool SEQ = false; };
+template <> struct TileCfg<256> { static constexpr int NW = 4, BC = 32, WPE = 2; static constexpr bool SEQ = true; };
 
 template <int D>
 struct Layout {
@@ -160,11 +165,17 @@ struct Layout {
   static constexpr int VROW = D * 2 + 64;      // padded LDS row pitch of V (bytes)
   static constexpr int KT = BC * KROW;         // bytes per K tile
   static constexpr int VT = BC * VROW;         // bytes per V tile
-  static constexpr int LDS = 2 * KT + 2 * VT;  // two K and two V buffers
+  // A tile is written by 64-slot (1 KB) direct-to-LDS loads spread evenly over the waves;
+  // each buffer is rounded up so that every wave issues the same number of whole loads
+  // (the slots past the tile receive zeros), which keeps the load code free of branches.
+  static constexpr int KPW = (KT / 16 + 64 * NW - 1) / (64 * NW);  // K loads per wave
+  static constexpr int VPW = (VT / 16 + 64 * NW - 1) / (64 * NW);  // V loads per wave
+  static constexpr int KBUF = KPW * NW * 1024, VBUF = VPW * NW * 1024;
+  static constexpr int LDS = 2 * KBUF + 2 * VBUF;  // two K and two V buffers
 };
 
 template <int D, bool CAUSAL, class T>
-__global__ void __launch_bounds__(TileCfg<D>::NW * 64)
+__global__ void __launch_bounds__(TileCfg<D>::NW * 64, TileCfg<D>::WPE)
 fwd_kernel(FwdParams p) {
   using x8 = typename T::x8;
   using x2 = typename T::x2;
@@ -176,16 +187,14 @@ fwd_kernel(FwdParams p) {
   constexpr int MT2 = D / 32;       // output tiles (32 head-dim rows each)
   constexpr int KS2 = BC / 16;      // GEMM2 k-steps (over keys)
   constexpr int CPR = D / 8;        // 16-byte chunks per K/V row
-  constexpr int RPP = NT / CPR;     // rows staged per pass of the workgroup
-  constexpr int LOADS = BC / RPP;   // staging passes per tile
   constexpr int KROW = L::KROW, VROW = L::VROW, KT = L::KT, VT = L::VT;
-  static_assert(NT % CPR == 0 && BC % RPP == 0, "tile chunks must divide over the workgroup");
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 
   // Two K and two V tile buffers as separate LDS objects: the loop's buffer parity is a
   // compile-time value, so the compiler can see that the direct-to-LDS loads of the next
   // tiles never touch the buffers being read and does not wait for them early.
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds0[KT], k_lds1[KT], v_lds0[VT], v_lds1[VT];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds0[L::KBUF], k_lds1[L::KBUF], v_lds0[L::VBUF],
+      v_lds1[L::VBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -220,6 +229,11 @@ fwd_kernel(FwdParams p) {
       u32x4 raw = *(const u32x4*)(qp + (16 * t + 8 * hh) * 2);
       qf[t] = __builtin_bit_cast(x8, raw);
     }
+    // zero scale: zero Q (and a unit c), so that masked scores stay -inf instead of -inf * 0
+    if (p.zero_scores) {
+#pragma unroll
+      for (int t = 0; t < KS1; ++t) qf[t] = x8{};
+    }
   }
 
   f32x16 acc[MT2];
@@ -233,12 +247,11 @@ fwd_kernel(FwdParams p) {
   // ---- K/V tiles: buffer loads straight into LDS (buffer_load ... lds). One instruction
   //      of a wave fills 64 consecutive 16-byte LDS slots (M0 base + 16 * lane); a padded row
   //      is KROW/16 (VROW/16) slots, so each lane maps its slot to (row, chunk) once, here.
-  //      Pad slots and rows past the last key get an offset beyond the buffer's range, which
-  //      loads zeros; lanes past the end of the tile are switched off. Every offset is in the
+  //      Pad slots, rows past the last key and slots past the tile (in the buffer's rounding)
+  //      get an offset beyond the buffer's range, which loads zeros. Every offset is in the
   //      per-lane voffset, which is what the hardware range check covers.
-  constexpr int KSL = KROW / 16, VSL = VROW / 16;            // slots per padded row
-  constexpr int KI = (BC * KSL + 63) / 64, VI = (BC * VSL + 63) / 64;  // instructions per tile
-  constexpr int KPW = (KI + NW - 1) / NW, VPW = (VI + NW - 1) / NW;    // per wave (at most)
+  constexpr int KSL = KROW / 16, VSL = VROW / 16;  // slots per padded row
+  constexpr int KPW = L::KPW, VPW = L::VPW;          // loads per wave and tile
   constexpr uint32_t OOB = 0x80000000u;
   const uint32_t kv_row = (uint32_t)p.Hkv * D * 2;  // bytes between consecutive tokens
   const uint8_t* kbase = p.k + ((size_t)b * Nk * p.Hkv + kvh) * (size_t)(D * 2);
@@ -257,28 +270,23 @@ fwd_kernel(FwdParams p) {
   }
 
   auto load_tile = [&](int tile, const uint8_t* gbase, uint8_t* ldst, const uint32_t* vo,
-                       auto ni_tag, auto sl_tag) {
-    constexpr int NI = decltype(ni_tag)::value, SL = decltype(sl_tag)::value;
+                       auto nw_tag) {
+    constexpr int NPW = decltype(nw_tag)::value;
     const int k0 = tile * BC;
     const uint32_t valid = (uint32_t)min(BC, Nk - k0) * kv_row;
     const auto rs = make_rsrc(gbase + (size_t)k0 * kv_row, valid);
 #pragma unroll
-    for (int n = 0; n < (NI + NW - 1) / NW; ++n) {
-      const int I = wv + NW * n;
-      if (I < NI) {
-        if (64 * I + 64 <= BC * SL || 64 * I + lane < BC * SL)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs, (__attribute__((address_space(3))) void*)(ldst + 1024 * I), 16, vo[n], 0, 0, 0);
-      }
-    }
+    for (int n = 0; n < NPW; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(ldst + 1024 * (wv + NW * n)), 16, vo[n], 0, 0, 0);
   };
   // `buf` is a literal in the main loop (so buffer addresses are constants) and j & 1 in the
   // diagonal/tail iterations.
   auto load_k = [&](int tile, int buf) {
-    load_tile(tile, kbase, buf ? k_lds1 : k_lds0, k_vo, IntC<KI>{}, IntC<KSL>{});
+    load_tile(tile, kbase, buf ? k_lds1 : k_lds0, k_vo, IntC<KPW>{});
   };
   auto load_v = [&](int tile, int buf) {
-    load_tile(tile, vbase, buf ? v_lds1 : v_lds0, v_vo, IntC<VI>{}, IntC<VSL>{});
+    load_tile(tile, vbase, buf ? v_lds1 : v_lds0, v_vo, IntC<VPW>{});
   };
 
   // ---- per-lane LDS read bases
@@ -291,34 +299,20 @@ fwd_kernel(FwdParams p) {
   const int grp = lane >> 4, gi = lane & 15;
   const int v_rd = (4 * (grp >> 1) + (gi >> 2)) * VROW + (2 * (grp & 1) + ((gi & 3) >> 1)) * 16 + (gi & 1) * 8;
 
-  // Back-to-back MFMAs that accumulate into the same registers issue at roughly half rate,
-  // so both products alternate between independent accumulators: GEMM1 between its score
-  // tiles (or, with a single score tile, between even and odd k-steps summed at the end),
-  // GEMM2 between its output tiles.
+  // GEMM1 walks the head dim with its score tiles innermost, GEMM2 the keys with its output
+  // tiles innermost (a dependent MFMA chain issues at nearly full rate on gfx950, so a single
+  // score tile needs no split accumulator).
   auto gemm1 = [&](int buf, f32x16 (&s)[MT1]) {
     const uint8_t* kl = (buf ? k_lds1 : k_lds0) + k_rd;
-    if constexpr (MT1 >= 2) {
 #pragma unroll
-      for (int mt = 0; mt < MT1; ++mt) s[mt] = f32x16{};
+    for (int mt = 0; mt < MT1; ++mt) s[mt] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < KS1; ++t)
+    for (int t = 0; t < KS1; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT1; ++mt) {
-          u32x4 raw = *(const u32x4*)(kl + mt * 32 * KROW + t * 32);
-          s[mt] = T::mfma(__builtin_bit_cast(x8, raw), qf[t], s[mt]);
-        }
-    } else {
-      f32x16 s_odd = f32x16{};
-      s[0] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < KS1; t += 2) {
-        u32x4 r0 = *(const u32x4*)(kl + t * 32);
-        u32x4 r1 = *(const u32x4*)(kl + (t + 1) * 32);
-        s[0] = T::mfma(__builtin_bit_cast(x8, r0), qf[t], s[0]);
-        s_odd = T::mfma(__builtin_bit_cast(x8, r1), qf[t + 1], s_odd);
+      for (int mt = 0; mt < MT1; ++mt) {
+        u32x4 raw = *(const u32x4*)(kl + mt * 32 * KROW + t * 32);
+        s[mt] = T::mfma(__builtin_bit_cast(x8, raw), qf[t], s[mt]);
       }
-      s[0] += s_odd;
-    }
   };
 
   auto gemm2 = [&](int buf, const x8 (&pf)[KS2], const x8* pl) {
@@ -412,6 +406,54 @@ fwd_kernel(FwdParams p) {
     lO += sumO;
   };
 
+  int nfull = Nk / BC;
+  if (CAUSAL) nfull = min(nfull, (q_wg0 + 1) / BC);
+
+  if constexpr (TileCfg<D>::SEQ) {
+  // ---- sequential tile loop. Iteration j: loads of K(j+1), V(j+1) in flight; S = Q K(j)^T;
+  //      mask (diagonal/tail tiles); rescale; softmax; O += P V(j); barrier.
+  auto seq_iteration = [&](const int j, const int par, auto split_tag, auto mask_tag) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    constexpr bool MASKED = decltype(mask_tag)::value;
+    if (j + 1 < ntiles) {
+      load_k(j + 1, 1 - par);
+      load_v(j + 1, 1 - par);
+    }
+    if (!MASKED || j < wtiles) {
+      f32x16 sc[MT1];
+      gemm1(par, sc);
+      if (MASKED) mask(j, sc);
+      rescale_to(rowmax(sc));
+      x8 pf[KS2];
+      x8 pl[SPLIT ? KS2 : 1];
+      softmax(sc, pf, SPLIT ? pl : nullptr);
+      gemm2(par, pf, SPLIT ? pl : nullptr);
+    }
+    __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
+  };
+  using F = BoolC<false>;
+  using U = BoolC<true>;
+  load_k(0, 0);
+  load_v(0, 0);
+  __syncthreads();
+  int j = 0;
+  if (nfull > 0) {
+    seq_iteration(0, 0, U{}, F{});
+    j = 1;
+    for (; j + 1 < nfull; j += 2) {
+      seq_iteration(j, 1, F{}, F{});
+      seq_iteration(j + 1, 0, F{}, F{});
+    }
+    if (j < nfull) {
+      seq_iteration(j, 1, F{}, F{});
+      ++j;
+    }
+  } else {
+    seq_iteration(0, 0, U{}, U{});
+    j = 1;
+  }
+  for (; j < ntiles; ++j) seq_iteration(j, j & 1, F{}, U{});
+  } else {
   // ---- prologue: K(0), V(0), K(1) into LDS, scores of tile 0
   load_k(0, 0);
   load_v(0, 0);
@@ -428,8 +470,6 @@ fwd_kernel(FwdParams p) {
   //      Tiles below `nfull` are visible to every query of the workgroup and inside Nk, so
   //      their iterations carry no masking code; the rest (diagonal and tail tiles) mask,
   //      and a wave whose queries all precede a tile skips that tile's math.
-  int nfull = Nk / BC;
-  if (CAUSAL) nfull = min(nfull, (q_wg0 + 1) / BC);
   // main iterations: unmasked and followed by a next tile
   const int nmain = min(nfull, ntiles - 1);
 
@@ -468,7 +508,7 @@ fwd_kernel(FwdParams p) {
   //   phase 2: each GEMM2(j) MFMA with the V read PF steps ahead and with one slice of the
   //            row max of tile j+1 (which the next iteration's rescale decision needs).
   // sched_barrier fences keep each step's instructions together.
-  constexpr int PF = 4;
+  constexpr int PF = D == 256 ? 2 : 4;  // LDS fragment reads issued this many MFMAs ahead
   constexpr int N1 = MT1 * KS1, N2 = MT2 * KS2;
   constexpr int NPAIR = 8 * MT1;  // score pairs per lane per tile
   auto main_iteration = [&](const int j, f32x16 (&sc)[MT1], f32x16 (&sn)[MT1], auto par_tag) {
@@ -480,7 +520,7 @@ fwd_kernel(FwdParams p) {
     const uint8_t* kl = (PAR ? k_lds0 : k_lds1) + k_rd;  // K(j+1): buffer 1 - PAR
     const uint8_t* vl = (PAR ? v_lds1 : v_lds0) + v_rd;  // V(j): buffer PAR
     auto kfrag = [&](const int i) -> x8 {
-      const int t = MT1 >= 2 ? i / MT1 : i, mt = MT1 >= 2 ? i % MT1 : 0;
+      const int t = i / MT1, mt = i % MT1;
       return __builtin_bit_cast(x8, *(const u32x4*)(kl + mt * 32 * KROW + t * 32));
     };
     auto vfrag = [&](const int i) -> x8 {
@@ -495,7 +535,6 @@ fwd_kernel(FwdParams p) {
       return __builtin_bit_cast(x8, raw);
     };
     x8 kf[N1], vf[N2], pf[KS2];
-    f32x16 s_odd;
     float sumL0 = 0.f, sumL1 = 0.f, sumO = 0.f;
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
@@ -506,32 +545,26 @@ fwd_kernel(FwdParams p) {
         kf[i + PF] = kfrag(i + PF);
       else
         vf[i + PF - N1] = vfrag(i + PF - N1);
-      if constexpr (MT1 >= 2) {
+      {
         const int t = i / MT1, mt = i % MT1;
         sn[mt] = T::mfma(kf[i], qf[t], t == 0 ? f32x16{} : sn[mt]);
-      } else if (i & 1) {
-        s_odd = T::mfma(kf[i], qf[i], i == 1 ? f32x16{} : s_odd);
-      } else {
-        sn[0] = T::mfma(kf[i], qf[i], i == 0 ? f32x16{} : sn[0]);
       }
       if ((i * NPAIR) % N1 == 0) {
+        // softmax of one pair: p overwrites its score (the sums are taken in phase 2)
         const int pi = i * NPAIR / N1, mt = pi / 8, r = (pi % 8) * 2;
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][r], c, negm));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][r + 1], c, negm));
-        sumL0 += p0;
-        sumL1 += p1;
+        sc[mt][r] = p0;
+        sc[mt][r + 1] = p1;
         const x2 pb = T::cvt2(p0, p1);
-        sumO = T::dot2(pb, one2, sumO);
         const int u = mt * 2 + (r >> 3);
         pf[u][(r & 7)] = pb[0];
         pf[u][(r & 7) + 1] = pb[1];
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    lL += sumL0 + sumL1;
-    lO += sumO;
     float mx = -__builtin_inff();
-    constexpr int VPS = (16 * MT1) / N2;  // next-tile scores folded into the max per step
+    constexpr int VPS = (16 * MT1) / N2;  // p values summed (and next-tile scores maxed) per step
 #pragma unroll
     for (int i = 0; i < N2; ++i) {
       if (i + PF < N2) vf[i + PF] = vfrag(i + PF);
@@ -539,11 +572,26 @@ fwd_kernel(FwdParams p) {
       acc[md] = T::mfma(vf[i], pf[u], acc[md]);
 #pragma unroll
       for (int e = i * VPS; e < (i + 1) * VPS; ++e) {
-        if constexpr (MT1 == 1) sn[0][e] += s_odd[e];
+        if (e & 1)
+          sumL1 += sc[e / 16][e % 16];
+        else
+          sumL0 += sc[e / 16][e % 16];
         mx = __builtin_fmaxf(mx, sn[e / 16][e % 16]);
       }
+      if ((i * NPAIR) % N2 == 0) {  // sum of the rounded pair that normalises O
+        const int pi = i * NPAIR / N2, mt = pi / 8, r = (pi % 8) * 2;
+        const int u2 = mt * 2 + (r >> 3);
+        x2 pb;
+        pb[0] = pf[u2][(r & 7)];
+        pb[1] = pf[u2][(r & 7) + 1];
+        sumO = T::dot2(pb, one2, sumO);
+      }
+      // keep this slice in this step (otherwise the reductions are sunk past the interleave)
+      asm volatile("" : "+v"(mx), "+v"(sumL0), "+v"(sumL1), "+v"(sumO));
       __builtin_amdgcn_sched_barrier(0);
     }
+    lL += sumL0 + sumL1;
+    lO += sumO;
     mx = __builtin_fmaxf(mx, other_half(mx));
     mt_cur = mx * c;
     __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
@@ -576,6 +624,7 @@ fwd_kernel(FwdParams p) {
     iteration(j, s_a, s_b, T0{}, T1{});
 #pragma unroll
     for (int mt = 0; mt < MT1; ++mt) s_a[mt] = s_b[mt];
+  }
   }
 
   // ---- epilogue: combine the two lane halves' sums, normalise, store O and LSE

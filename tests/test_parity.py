@@ -60,9 +60,10 @@ def _compare(name, o, lse, O_ref, L_ref, rows=None):
         f"{name}: O max {mx:.3e} (|O|<4 {mx_small:.3e}, excess {ex_big:.3e}) mean {mean:.3e} LSE max {lmx:.3e}"
 
 
-def _run_full(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, k_spike=False):
+def _run_full(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, k_spike=False, scale=None):
     q, k, v = W.make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, dtype=dtype, k_spike=k_spike)
-    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
     _say(f"[gpu] {name} B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} {dtype} seed={seed}")
     o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
     torch.cuda.synchronize()
@@ -129,6 +130,14 @@ def test_workload_sampled_rows(w):
         O_ref, L_ref = attention_ref(q, k, v, causal, w.scale, rows=rows)
         _compare(f"{w.name}/{'causal' if causal else 'noncausal'}", o, lse, O_ref, L_ref, rows=rows)
         del o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_zero_scale(d, causal):
+    # scale 0: every visible key gets the same weight (O = mean of the visible V rows,
+    # LSE = ln(number of visible keys)); 257 keys leave a masked tail in the last tile
+    _run_full(f"zero_scale_d{d}", 1, 257, 257, 2, 1, d, causal, 70 + d, scale=0.0)
 
 
 @pytest.mark.parametrize("w", [W.tiny(), W.ragged()], ids=["tiny", "ragged"])

@@ -26,12 +26,13 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _run(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, head=None):
+def _run(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, head=None, scale=None):
     """head=(b, kvh): compare only that KV head's group (dq of its query heads, its dk, dv)."""
     q, k, v = W.make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, dtype=dtype)
     g = torch.Generator().manual_seed(seed + 7)
     do = torch.randn((B, Nq, Hq, d), generator=g).to(dtype)
-    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
     _say(f"[gpu] bwd {name} B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} {dtype}")
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
@@ -51,8 +52,11 @@ def _run(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, head=N
         assert np.isfinite(got).all(), f"{name}/{tname}: non-finite"
         err = np.abs(got - ref)
         mx, mean, rmax, rmean = err.max(), err.mean(), np.abs(ref).max(), np.abs(ref).mean()
-        _say(f"  {name}/{tname}: max err {mx:.3e} (max|ref| {rmax:.3e}, ratio {mx / rmax:.2e}) "
-             f"mean err {mean:.3e} (mean|ref| {rmean:.3e}, ratio {mean / rmean:.2e})")
+        _say(f"  {name}/{tname}: max err {mx:.3e} (max|ref| {rmax:.3e}, ratio {mx / max(rmax, 1e-300):.2e}) "
+             f"mean err {mean:.3e} (mean|ref| {rmean:.3e}, ratio {mean / max(rmean, 1e-300):.2e})")
+        if rmax == 0.0:  # a gradient that is exactly zero (dq, dk at scale 0)
+            assert mx == 0.0, f"{name}/{tname}"
+            continue
         assert mx <= MAX_REL * rmax and mean <= MEAN_REL * rmean, f"{name}/{tname}"
 
 
@@ -84,6 +88,12 @@ def test_bwd_rectangular(case):
 @pytest.mark.parametrize("d", [128, 256])
 def test_bwd_fp16(d):
     _run(f"fp16_d{d}", 1, 300, 300, 2, 1, d, True, 69 + d, dtype=torch.float16)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_zero_scale(d):
+    # scale 0: P is uniform over the visible keys, dq = dk = 0 exactly, dv = P^T dO
+    _run(f"zero_scale_d{d}", 1, 257, 257, 2, 1, d, True, 80 + d, scale=0.0)
 
 
 FULL_BWD = [W.by_name(n) for n in ("hd128_N8192_mha", "hd128_N8192_gqa4", "hd256_N8192")]
