@@ -150,12 +150,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base,
 
 // Tile configuration per head dim: waves per workgroup, keys per K/V tile.
 template <int D> struct TileCfg;
-// SEQ: one score buffer and a plain per-tile order (two workgroups share a CU and overlap
-// each other); otherwise the scores of the next tile are computed during the softmax of the
-// current one (one workgroup per CU, explicit MFMA/VALU interleave). WPE: waves per SIMD
-// the register budget is sized for.
-template <> struct TileCfg<128> { static constexpr int NW = 8, BC = 64, WPE = 2; static constexpr bool SEQ = false; };
-template <> struct TileCfg<256> { static constexpr int NW = 4, BC = 32, WPE = 2; static constexpr bool SEQ = true; };
+// Loop schedules (MODE):
+//   PIPE: the scores of the next tile are computed during the softmax of the current one,
+//         with an explicit MFMA/VALU interleave inside each wave (one workgroup per CU);
+//   SEQ:  one score buffer and a plain per-tile order; two workgroups share a CU and their
+//         waves overlap each other (hd256: O alone takes half of a wave's 256 registers, so
+//         a second score buffer does not fit at two waves per SIMD).
+// WPE: waves per SIMD the register budget is sized for.
+enum LoopMode { PIPE = 0, SEQ = 1 };
+template <> struct TileCfg<128> { static constexpr int NW = 8, BC = 64, WPE = 2, MODE = PIPE; };
+template <> struct TileCfg<256> { static constexpr int NW = 4, BC = 32, WPE = 2, MODE = SEQ; };
 
 template <int D>
 struct Layout {
@@ -165,12 +169,14 @@ struct Layout {
   static constexpr int VROW = D * 2 + 64;      // padded LDS row pitch of V (bytes)
   static constexpr int KT = BC * KROW;         // bytes per K tile
   static constexpr int VT = BC * VROW;         // bytes per V tile
-  // A tile is written by 64-slot (1 KB) direct-to-LDS loads spread evenly over the waves;
-  // each buffer is rounded up so that every wave issues the same number of whole loads
-  // (the slots past the tile receive zeros), which keeps the load code free of branches.
-  static constexpr int KPW = (KT / 16 + 64 * NW - 1) / (64 * NW);  // K loads per wave
-  static constexpr int VPW = (VT / 16 + 64 * NW - 1) / (64 * NW);  // V loads per wave
-  static constexpr int KBUF = KPW * NW * 1024, VBUF = VPW * NW * 1024;
+  // A tile is written by 64-slot (1 KB) direct-to-LDS loads spread evenly over the NL
+  // loading waves; each buffer is rounded up so that every loading wave issues the same
+  // number of whole loads (the slots past the tile receive zeros), which keeps the load
+  // code free of branches.
+  static constexpr int NL = NW;
+  static constexpr int KPW = (KT / 16 + 64 * NL - 1) / (64 * NL);  // K loads per loading wave
+  static constexpr int VPW = (VT / 16 + 64 * NL - 1) / (64 * NL);  // V loads per loading wave
+  static constexpr int KBUF = KPW * NL * 1024, VBUF = VPW * NL * 1024;
   static constexpr int LDS = 2 * KBUF + 2 * VBUF;  // two K and two V buffers
 };
 
@@ -251,7 +257,7 @@ fwd_kernel(FwdParams p) {
   //      get an offset beyond the buffer's range, which loads zeros. Every offset is in the
   //      per-lane voffset, which is what the hardware range check covers.
   constexpr int KSL = KROW / 16, VSL = VROW / 16;  // slots per padded row
-  constexpr int KPW = L::KPW, VPW = L::VPW;          // loads per wave and tile
+  constexpr int NL = L::NL, KPW = L::KPW, VPW = L::VPW;  // loading waves, loads per wave and tile
   constexpr uint32_t OOB = 0x80000000u;
   const uint32_t kv_row = (uint32_t)p.Hkv * D * 2;  // bytes between consecutive tokens
   const uint8_t* kbase = p.k + ((size_t)b * Nk * p.Hkv + kvh) * (size_t)(D * 2);
@@ -260,12 +266,12 @@ fwd_kernel(FwdParams p) {
   uint32_t k_vo[KPW], v_vo[VPW];
 #pragma unroll
   for (int n = 0; n < KPW; ++n) {
-    const int slot = 64 * (wv + NW * n) + lane, row = slot / KSL, ch = slot % KSL;
+    const int slot = 64 * (wv + NL * n) + lane, row = slot / KSL, ch = slot % KSL;
     k_vo[n] = (ch < CPR && row < BC) ? (uint32_t)row * kv_row + ch * 16 : OOB;
   }
 #pragma unroll
   for (int n = 0; n < VPW; ++n) {
-    const int slot = 64 * (wv + NW * n) + lane, row = slot / VSL, ch = slot % VSL;
+    const int slot = 64 * (wv + NL * n) + lane, row = slot / VSL, ch = slot % VSL;
     v_vo[n] = (ch < CPR && row < BC) ? (uint32_t)row * kv_row + ch * 16 : OOB;
   }
 
@@ -278,7 +284,7 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int n = 0; n < NPW; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(ldst + 1024 * (wv + NW * n)), 16, vo[n], 0, 0, 0);
+          rs, (__attribute__((address_space(3))) void*)(ldst + 1024 * (wv + NL * n)), 16, vo[n], 0, 0, 0);
   };
   // `buf` is a literal in the main loop (so buffer addresses are constants) and j & 1 in the
   // diagonal/tail iterations.
@@ -409,7 +415,7 @@ fwd_kernel(FwdParams p) {
   int nfull = Nk / BC;
   if (CAUSAL) nfull = min(nfull, (q_wg0 + 1) / BC);
 
-  if constexpr (TileCfg<D>::SEQ) {
+  if constexpr (TileCfg<D>::MODE == SEQ) {
   // ---- sequential tile loop. Iteration j: loads of K(j+1), V(j+1) in flight; S = Q K(j)^T;
   //      mask (diagonal/tail tiles); rescale; softmax; O += P V(j); barrier.
   auto seq_iteration = [&](const int j, const int par, auto split_tag, auto mask_tag) {
