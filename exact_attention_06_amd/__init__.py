@@ -2,9 +2,15 @@
 
     o, lse = forward(q, k, v, causal=False, scale=None)
     dq, dk, dv = backward(q, k, v, o, lse, dout, causal=False, scale=None)
+    o, lse = forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False,
+                            scale=None, seqused_k=None)
+    o, lse = forward_paged(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
+                           max_seqlen_q, causal=False, scale=None)
 
 q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] (bf16 or fp16, contiguous, on the GPU);
-returns o [B, Nq, Hq, d] (same dtype) and lse [B, Hq, Nq] (fp32). torch provides device
+returns o [B, Nq, Hq, d] (same dtype) and lse [B, Hq, Nq] (fp32). The variable-length
+forms take packed q [total_q, Hq, d] and return o like q and lse [Hq, total_q]; their causal
+mask is aligned bottom-right (see include/fa_fwd.h). torch provides device
 memory and the current stream; the computation is entirely the library's HIP kernels.
 Contract violations raise (ValueError for arguments, RuntimeError for launch failures);
 nothing falls back to another implementation.
@@ -16,7 +22,7 @@ import math
 
 from . import _lib
 
-__all__ = ["forward", "backward", "check_args", "FaError"]
+__all__ = ["forward", "backward", "forward_varlen", "forward_paged", "check_args", "FaError"]
 
 
 class FaError(ValueError):
@@ -133,3 +139,109 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if rc != 0:
         _raise(rc)
     return dq, dk, dv
+
+
+def _int32_vec(name, t, n, torch, device):
+    _check_tensor(name, t, torch)
+    if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n:
+        raise ValueError(f"{name} must be a 1-D int32 tensor with {n} entries")
+    if t.device != device:
+        raise ValueError(f"{name} must be on the device of q")
+
+
+def _varlen_common(q, kv_tensors, torch, lib, bf16_fn, f16_fn):
+    for name, t in (("q", q),) + kv_tensors:
+        _check_tensor(name, t, torch)
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    if any(t.dtype != q.dtype for _, t in kv_tensors):
+        raise ValueError("q, k and v must share one dtype")
+    if q.dtype == torch.bfloat16:
+        return getattr(lib, bf16_fn)
+    if q.dtype == torch.float16:
+        return getattr(lib, f16_fn)
+    raise ValueError("dtype must be bfloat16 or float16")
+
+
+def _varlen_out(q, out, lse, torch):
+    total_q, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (Hq, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor [Hq, total_q]")
+    return out, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
+                   scale: float | None = None, seqused_k=None, out=None, lse=None):
+    """Packed variable-length forward (fa_fwd_varlen): q [total_q, Hq, d], k/v [total_k, Hkv, d],
+    cu_seqlens_q / cu_seqlens_k int32 [B+1], seqused_k None or int32 [B]. Returns
+    o [total_q, Hq, d] and lse [Hq, total_q] (fp32)."""
+    import torch
+
+    lib = _lib.load()
+    fn = _varlen_common(q, (("k", k), ("v", v)), torch, lib, "fa_fwd_varlen", "fa_fwd_varlen_f16")
+    if q.dim() != 3 or k.dim() != 3 or tuple(v.shape) != tuple(k.shape) or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, _ = k.shape
+    B = cu_seqlens_q.shape[0] - 1 if isinstance(cu_seqlens_q, torch.Tensor) else -1
+    _int32_vec("cu_seqlens_q", cu_seqlens_q, B + 1, torch, q.device)
+    _int32_vec("cu_seqlens_k", cu_seqlens_k, B + 1, torch, q.device)
+    if seqused_k is not None:
+        _int32_vec("seqused_k", seqused_k, B, torch, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _varlen_out(q, out, lse, torch)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                0 if seqused_k is None else seqused_k.data_ptr(), B, int(max_seqlen_q), total_q, total_k,
+                Hq, Hkv, d, int(bool(causal)), float(scale), stream)
+    if rc != 0:
+        _raise(rc)
+    return out, lse
+
+
+def forward_paged(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table, max_seqlen_q: int,
+                  causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Forward against a paged K/V cache (fa_fwd_paged): q [total_q, Hq, d],
+    k_cache/v_cache [num_pages, page_size, Hkv, d], cu_seqlens_q int32 [B+1], seqused_k
+    int32 [B], block_table int32 [B, max_pages]. Returns o [total_q, Hq, d] and
+    lse [Hq, total_q] (fp32)."""
+    import torch
+
+    lib = _lib.load()
+    fn = _varlen_common(q, (("k_cache", k_cache), ("v_cache", v_cache)), torch, lib, "fa_fwd_paged",
+                        "fa_fwd_paged_f16")
+    if (q.dim() != 3 or k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape)
+            or k_cache.shape[3] != q.shape[2]):
+        raise ValueError("q must be [total_q, Hq, d] and k_cache, v_cache [num_pages, page_size, Hkv, d]")
+    total_q, Hq, d = q.shape
+    num_pages, page_size, Hkv, _ = k_cache.shape
+    B = cu_seqlens_q.shape[0] - 1 if isinstance(cu_seqlens_q, torch.Tensor) else -1
+    _int32_vec("cu_seqlens_q", cu_seqlens_q, B + 1, torch, q.device)
+    _int32_vec("seqused_k", seqused_k, B, torch, q.device)
+    _check_tensor("block_table", block_table, torch)
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be an int32 tensor [B, max_pages]")
+    if block_table.device != q.device:
+        raise ValueError("block_table must be on the device of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _varlen_out(q, out, lse, torch)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                cu_seqlens_q.data_ptr(), seqused_k.data_ptr(), block_table.data_ptr(), B, int(max_seqlen_q),
+                total_q, num_pages, page_size, block_table.shape[1], Hq, Hkv, d, int(bool(causal)),
+                float(scale), stream)
+    if rc != 0:
+        _raise(rc)
+    return out, lse

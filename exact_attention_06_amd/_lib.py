@@ -24,6 +24,7 @@ FA_ERR_ALIGN = -6
 FA_ERR_TOO_LARGE = -7
 FA_ERR_LAUNCH = -8
 FA_ERR_WORKSPACE = -9
+FA_ERR_PAGE = -10
 
 _lib = None
 
@@ -31,6 +32,11 @@ _I = ctypes.c_int
 _P = ctypes.c_void_p
 _FWD_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 _CHECK_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float]
+# q, k, v, o, lse, cu_q, cu_k, seqused, B, max_seqlen_q, total_q, total_k, Hq, Hkv, d, causal, scale, stream
+_VARLEN_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+# q, kc, vc, o, lse, cu_q, seqused, block_table, B, max_seqlen_q, total_q, num_pages, page_size,
+# max_pages, Hq, Hkv, d, causal, scale, stream
+_PAGED_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 _BWD_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _I, _I, _I,
              ctypes.c_float, _P]
 
@@ -46,6 +52,12 @@ def load():
             fn = getattr(lib, name)
             fn.argtypes = _FWD_ARGS
             fn.restype = _I
+        for names, args in ((("fa_fwd_varlen", "fa_fwd_varlen_f16"), _VARLEN_ARGS),
+                            (("fa_fwd_paged", "fa_fwd_paged_f16"), _PAGED_ARGS)):
+            for name in names:
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = _I
         for name in ("fa_bwd", "fa_bwd_f16"):
             fn = getattr(lib, name)
             fn.argtypes = _BWD_ARGS

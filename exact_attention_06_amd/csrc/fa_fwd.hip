@@ -14,12 +14,29 @@
 
 namespace {
 
-template <int D, bool CAUSAL, class T>
+template <int D, bool CAUSAL, class T, bool VAR>
 int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
   using L = fa::Layout<D>;
   // the kernel's K/V buffers are static LDS (L::LDS bytes, within gfx950's 160 KB per CU)
-  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, T>), dim3(grid), dim3(L::NW * 64), 0, stream, prm);
+  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, T, VAR>), dim3(grid), dim3(L::NW * 64), 0, stream, prm);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// Scale: a zero (or subnormal) scale makes every visible score exactly 0; the kernel then
+// zeroes Q and uses c = log2(e), since -inf * 0 would turn masked scores into NaN.
+void set_scale(fa::FwdParams& prm, float scale) {
+  prm.zero_scores = !(scale * fa::LOG2E >= FLT_MIN);
+  prm.c = prm.zero_scores ? fa::LOG2E : scale * fa::LOG2E;
+}
+
+template <bool VAR, class T>
+int dispatch(fa::FwdParams& prm, int d, int causal, hipStream_t s) {
+  const int BR = d == 128 ? fa::Layout<128>::BR : fa::Layout<256>::BR;
+  prm.nqt = (prm.Nq + BR - 1) / BR;
+  const int grid = prm.B * prm.Hq * prm.nqt;
+  if (d == 128)
+    return causal ? launch<128, true, T, VAR>(prm, grid, s) : launch<128, false, T, VAR>(prm, grid, s);
+  return causal ? launch<256, true, T, VAR>(prm, grid, s) : launch<256, false, T, VAR>(prm, grid, s);
 }
 
 template <int D> int br() { return fa::Layout<D>::BR; }
@@ -57,17 +74,68 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   prm.Hq = Hq;
   prm.Hkv = Hkv;
   prm.group = Hq / Hkv;
-  // A zero (or subnormal) scale makes every visible score exactly 0; the kernel then zeroes
-  // Q and uses c = log2(e), since -inf * 0 would turn masked scores into NaN.
-  prm.zero_scores = !(scale * fa::LOG2E >= FLT_MIN);
-  prm.c = prm.zero_scores ? fa::LOG2E : scale * fa::LOG2E;
-  const int BR = d == 128 ? br<128>() : br<256>();
-  prm.nqt = (Nq + BR - 1) / BR;
-  const int grid = B * Hq * prm.nqt;
-  hipStream_t s = (hipStream_t)stream;
-  if (d == 128)
-    return causal ? launch<128, true, T>(prm, grid, s) : launch<128, false, T>(prm, grid, s);
-  return causal ? launch<256, true, T>(prm, grid, s) : launch<256, false, T>(prm, grid, s);
+  prm.cu_q = prm.cu_k = prm.seqused = prm.block_table = nullptr;
+  prm.total_q = prm.total_k = prm.page_size = prm.max_pages = prm.num_pages = 0;
+  set_scale(prm, scale);
+  return dispatch<false, T>(prm, d, causal, (hipStream_t)stream);
+}
+
+// Variable-length forward (packed K/V when block_table is NULL, else paged K/V).
+int check_var(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const int* cu_q, const int* cu_k, const int* seqused, const int* block_table, int B,
+              int max_seqlen_q, int total_q, int total_k, int num_pages, int page_size, int max_pages,
+              int Hq, int Hkv, int d, float scale, bool paged) {
+  if (!q || !k || !v || !o || !lse || !cu_q) return FA_ERR_NULL;
+  if (paged ? (!seqused || !block_table) : !cu_k) return FA_ERR_NULL;
+  if (B <= 0 || max_seqlen_q <= 0 || total_q <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return FA_ERR_SHAPE;
+  if (!paged && total_k < 0) return FA_ERR_SHAPE;
+  if (paged && (page_size <= 0 || page_size % 64 != 0 || num_pages <= 0 || max_pages <= 0 ||
+                (int64_t)max_pages * page_size > INT_MAX || (int64_t)num_pages * page_size > INT_MAX))
+    return FA_ERR_PAGE;
+  if (d != 128 && d != 256) return FA_ERR_HEADDIM;
+  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)cu_q | (uintptr_t)cu_k | (uintptr_t)seqused | (uintptr_t)block_table) & 3)
+    return FA_ERR_ALIGN;
+  const int64_t BR = d == 128 ? br<128>() : br<256>();
+  const int64_t grid = (int64_t)B * Hq * ((max_seqlen_q + BR - 1) / BR);
+  if (grid > INT_MAX || (int64_t)max_seqlen_q + BR > INT_MAX || (int64_t)B * Hq > INT_MAX)
+    return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+template <class T>
+int run_var(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_q,
+            const int* cu_k, const int* seqused, const int* block_table, int B, int max_seqlen_q,
+            int total_q, int total_k, int num_pages, int page_size, int max_pages, int Hq, int Hkv,
+            int d, int causal, float scale, void* stream, bool paged) {
+  const int st = check_var(q, k, v, o, lse, cu_q, cu_k, seqused, block_table, B, max_seqlen_q, total_q,
+                           total_k, num_pages, page_size, max_pages, Hq, Hkv, d, scale, paged);
+  if (st != FA_OK) return st;
+  fa::FwdParams prm;
+  prm.q = (const uint8_t*)q;
+  prm.k = (const uint8_t*)k;
+  prm.v = (const uint8_t*)v;
+  prm.o = (uint8_t*)o;
+  prm.lse = lse;
+  prm.B = B;
+  prm.Nq = max_seqlen_q;  // sizes the grid; each block reads its own sequence's length
+  prm.Nk = 0;
+  prm.Hq = Hq;
+  prm.Hkv = Hkv;
+  prm.group = Hq / Hkv;
+  prm.cu_q = cu_q;
+  prm.cu_k = paged ? nullptr : cu_k;
+  prm.seqused = seqused;
+  prm.block_table = paged ? block_table : nullptr;
+  prm.total_q = total_q;
+  prm.total_k = paged ? 0 : total_k;
+  prm.page_size = paged ? page_size : 0;
+  prm.max_pages = paged ? max_pages : 0;
+  prm.num_pages = paged ? num_pages : 0;
+  set_scale(prm, scale);
+  return dispatch<true, T>(prm, d, causal, (hipStream_t)stream);
 }
 
 size_t bwd_ws_bytes(int B, int Nq, int Hq) {
@@ -147,6 +215,38 @@ int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
   return run<fa::F16>(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale, stream);
 }
 
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, const int* seqused_k, int B, int max_seqlen_q, int total_q,
+                  int total_k, int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  return run_var<fa::Bf16>(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, seqused_k, nullptr, B, max_seqlen_q,
+                           total_q, total_k, 0, 0, 0, Hq, Hkv, d, causal, scale, stream, false);
+}
+
+int fa_fwd_varlen_f16(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
+                      const int* cu_seqlens_k, const int* seqused_k, int B, int max_seqlen_q, int total_q,
+                      int total_k, int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  return run_var<fa::F16>(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, seqused_k, nullptr, B, max_seqlen_q,
+                          total_q, total_k, 0, 0, 0, Hq, Hkv, d, causal, scale, stream, false);
+}
+
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                 const int* cu_seqlens_q, const int* seqused_k, const int* block_table, int B, int max_seqlen_q,
+                 int total_q, int num_pages, int page_size, int max_pages, int Hq, int Hkv, int d, int causal,
+                 float scale, void* stream) {
+  return run_var<fa::Bf16>(q, k_cache, v_cache, o, lse, cu_seqlens_q, nullptr, seqused_k, block_table, B,
+                           max_seqlen_q, total_q, 0, num_pages, page_size, max_pages, Hq, Hkv, d, causal, scale,
+                           stream, true);
+}
+
+int fa_fwd_paged_f16(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                     const int* cu_seqlens_q, const int* seqused_k, const int* block_table, int B,
+                     int max_seqlen_q, int total_q, int num_pages, int page_size, int max_pages, int Hq, int Hkv,
+                     int d, int causal, float scale, void* stream) {
+  return run_var<fa::F16>(q, k_cache, v_cache, o, lse, cu_seqlens_q, nullptr, seqused_k, block_table, B,
+                          max_seqlen_q, total_q, 0, num_pages, page_size, max_pages, Hq, Hkv, d, causal, scale,
+                          stream, true);
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Nq, int Hq) { return bwd_ws_bytes(B, Nq, Hq); }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -175,6 +275,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_TOO_LARGE: return "problem too large for 32-bit grid or sequence indexing";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
     case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or smaller than fa_bwd_workspace_bytes";
+    case FA_ERR_PAGE: return "paged K/V: page_size must be a positive multiple of 64, num_pages and max_pages positive";
     default: return "unknown fa status code";
   }
 }

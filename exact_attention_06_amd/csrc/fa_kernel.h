@@ -103,6 +103,17 @@ struct FwdParams {
   int nqt;        // query tiles per (b, h)
   float c;        // scale * log2(e); log2(e) when zero_scores is set
   int zero_scores;  // scale is zero (or below the normal range): every score is exactly 0
+  // variable-length batches (kernel variant VAR): packed q/o rows of sequence b are
+  // cu_q[b] .. cu_q[b+1]-1; keys are packed rows cu_k[b] .. cu_k[b+1]-1 or, with a page
+  // table, logical key t of sequence b is row t % page_size of page
+  // block_table[b * max_pages + t / page_size]; seqused (optional for packed keys) limits
+  // the keys of sequence b. Nq is then the longest query length (it sizes the grid).
+  const int* cu_q;
+  const int* cu_k;
+  const int* seqused;
+  const int* block_table;
+  int total_q, total_k;
+  int page_size, max_pages, num_pages;
 };
 
 template <bool V> struct BoolC { static constexpr bool value = V; };
@@ -180,7 +191,7 @@ struct Layout {
   static constexpr int LDS = 2 * KBUF + 2 * VBUF;  // two K and two V buffers
 };
 
-template <int D, bool CAUSAL, class T>
+template <int D, bool CAUSAL, class T, bool VAR>
 __global__ void __launch_bounds__(TileCfg<D>::NW * 64, TileCfg<D>::WPE)
 fwd_kernel(FwdParams p) {
   using x8 = typename T::x8;
@@ -213,23 +224,73 @@ fwd_kernel(FwdParams p) {
   const int b = bh / p.Hq;
   const int hq = bh - b * p.Hq;
   const int kvh = hq / p.group;
-  const int Nq = p.Nq, Nk = p.Nk;
+
+  // ---- this block's sequence: query rows q_row0 .. q_row0 + Nq - 1 of the q/o tensors and
+  //      Nk keys. Dense: sequence b of a [B, Nq, H, d] batch. VAR: packed rows (bounds are
+  //      clamped to the tensors, so bad offsets cannot reach outside them). Causal: query i
+  //      sees keys j <= i + cshift, aligned bottom-right (cshift = 0 when Nq == Nk).
+  int Nq, Nk;
+  size_t q_row0, lse0;  // first q/o row; LSE index of (this head, row 0)
+  const uint8_t* kbase;
+  const uint8_t* vbase;
+  const size_t head_off = (size_t)kvh * (D * 2);
+  if constexpr (!VAR) {
+    Nq = p.Nq;
+    Nk = p.Nk;
+    q_row0 = (size_t)b * Nq;
+    lse0 = ((size_t)b * p.Hq + hq) * Nq;
+    kbase = p.k + (size_t)b * Nk * p.Hkv * (D * 2) + head_off;
+    vbase = p.v + (size_t)b * Nk * p.Hkv * (D * 2) + head_off;
+  } else {
+    const int q0 = min(max(p.cu_q[b], 0), p.total_q);
+    const int q1 = min(max(p.cu_q[b + 1], q0), p.total_q);
+    Nq = q1 - q0;
+    q_row0 = q0;
+    lse0 = (size_t)hq * p.total_q + q0;
+    if (p.block_table == nullptr) {
+      const int k0 = min(max(p.cu_k[b], 0), p.total_k);
+      const int k1 = min(max(p.cu_k[b + 1], k0), p.total_k);
+      Nk = k1 - k0;
+      kbase = p.k + (size_t)k0 * p.Hkv * (D * 2) + head_off;
+      vbase = p.v + (size_t)k0 * p.Hkv * (D * 2) + head_off;
+    } else {
+      Nk = p.max_pages * p.page_size;  // page bases are added per tile
+      kbase = p.k + head_off;
+      vbase = p.v + head_off;
+    }
+    if (p.seqused != nullptr) Nk = min(Nk, max(p.seqused[b], 0));
+  }
+  const int cshift = CAUSAL ? Nk - Nq : 0;
 
   const int q_wg0 = qt * BR;
+  if (VAR && q_wg0 >= Nq) return;  // a query tile past the end of this sequence
   const int qw0 = q_wg0 + wave * 32;
   const int q_lane = qw0 + l32;
   const int q_ld = q_lane < Nq ? q_lane : Nq - 1;
 
   int kend = Nk;
-  if (CAUSAL) kend = min(Nk, min(Nq, q_wg0 + BR));
+  if (CAUSAL) kend = min(Nk, min(Nq, q_wg0 + BR) + cshift);
   const int ntiles = (kend + BC - 1) / BC;
-  // tiles this wave computes on (causal: keys up to its last query; at least tile 0)
-  const int wtiles = CAUSAL ? max(1, min(ntiles, (min(qw0 + 32, Nq) + BC - 1) / BC)) : ntiles;
+  // tiles this wave computes on (causal: keys up to its last query). Dense: at least tile 0;
+  // VAR: a wave whose rows see no key at all has none.
+  const int wtiles = CAUSAL ? max(VAR ? 0 : 1, min(ntiles, (min(qw0 + 32, Nq) + cshift + BC - 1) / BC))
+                            : ntiles;
+  if (VAR && kend <= 0) {  // no row of this block sees a key: O = 0, LSE = -inf
+    if (q_lane < Nq) {
+      uint8_t* op = p.o + ((q_row0 + q_lane) * p.Hq + hq) * (size_t)(D * 2);
+#pragma unroll
+      for (int md = 0; md < MT2; ++md)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x2*)(op + (32 * md + 8 * i + 4 * hh) * 2) = u32x2{0u, 0u};
+      if (hh == 0) p.lse[lse0 + q_lane] = -__builtin_inff();
+    }
+    return;
+  }
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q_ld, dims 16t + 8hh .. +7
   x8 qf[KS1];
   {
-    const uint8_t* qp = p.q + (((size_t)b * Nq + q_ld) * p.Hq + hq) * (size_t)(D * 2);
+    const uint8_t* qp = p.q + ((q_row0 + q_ld) * p.Hq + hq) * (size_t)(D * 2);
 #pragma unroll
     for (int t = 0; t < KS1; ++t) {
       u32x4 raw = *(const u32x4*)(qp + (16 * t + 8 * hh) * 2);
@@ -260,8 +321,6 @@ fwd_kernel(FwdParams p) {
   constexpr int NL = L::NL, KPW = L::KPW, VPW = L::VPW;  // loading waves, loads per wave and tile
   constexpr uint32_t OOB = 0x80000000u;
   const uint32_t kv_row = (uint32_t)p.Hkv * D * 2;  // bytes between consecutive tokens
-  const uint8_t* kbase = p.k + ((size_t)b * Nk * p.Hkv + kvh) * (size_t)(D * 2);
-  const uint8_t* vbase = p.v + ((size_t)b * Nk * p.Hkv + kvh) * (size_t)(D * 2);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint32_t k_vo[KPW], v_vo[VPW];
 #pragma unroll
@@ -279,8 +338,17 @@ fwd_kernel(FwdParams p) {
                        auto nw_tag) {
     constexpr int NPW = decltype(nw_tag)::value;
     const int k0 = tile * BC;
-    const uint32_t valid = (uint32_t)min(BC, Nk - k0) * kv_row;
-    const auto rs = make_rsrc(gbase + (size_t)k0 * kv_row, valid);
+    const uint8_t* tbase = gbase + (size_t)k0 * kv_row;
+    int rows = min(BC, Nk - k0);
+    if constexpr (VAR) {
+      if (p.block_table != nullptr) {  // a tile lies inside one page (page_size % BC == 0)
+        const int lp = k0 / p.page_size;
+        const int pg = p.block_table[(size_t)b * p.max_pages + lp];
+        tbase = gbase + ((size_t)pg * p.page_size + (k0 - lp * p.page_size)) * kv_row;
+        if (pg < 0 || pg >= p.num_pages) rows = 0;  // not a page of the cache: zeros, no access
+      }
+    }
+    const auto rs = make_rsrc(tbase, (uint32_t)rows * kv_row);
 #pragma unroll
     for (int n = 0; n < NPW; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -347,9 +415,9 @@ fwd_kernel(FwdParams p) {
   // is visible iff its compile-time offset 32mt + 8(r/4) + r%4 is <= one per-lane limit.
   auto mask = [&](int j, f32x16 (&s)[MT1]) {
     const int k0 = j * BC;
-    const bool need = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > qw0));
+    const bool need = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > qw0 + cshift));
     if (need) {
-      const int last = CAUSAL ? min(q_lane, Nk - 1) : Nk - 1;  // last visible key
+      const int last = CAUSAL ? min(q_lane + cshift, Nk - 1) : Nk - 1;  // last visible key
       const int lim = last - k0 - 4 * hh;
 #pragma unroll
       for (int mt = 0; mt < MT1; ++mt)
@@ -413,7 +481,7 @@ fwd_kernel(FwdParams p) {
   };
 
   int nfull = Nk / BC;
-  if (CAUSAL) nfull = min(nfull, (q_wg0 + 1) / BC);
+  if (CAUSAL) nfull = max(0, min(nfull, (q_wg0 + 1 + cshift) / BC));
 
   if constexpr (TileCfg<D>::MODE == SEQ) {
   // ---- sequential tile loop. Iteration j: loads of K(j+1), V(j+1) in flight; S = Q K(j)^T;
@@ -637,8 +705,15 @@ fwd_kernel(FwdParams p) {
   lL += other_half(lL);
   lO += other_half(lO);
   if (q_lane < Nq) {
+    // VAR, causal: a row that sees no key (q_lane + cshift < 0) stores O = 0, LSE = -inf
+    const bool empty = VAR && CAUSAL && q_lane + cshift < 0;
+    if (empty) {
+      lO = 1.f;
+#pragma unroll
+      for (int md = 0; md < MT2; ++md) acc[md] = f32x16{};
+    }
     const float inv = 1.0f / lO;
-    uint8_t* op = p.o + (((size_t)b * Nq + q_lane) * p.Hq + hq) * (size_t)(D * 2);
+    uint8_t* op = p.o + ((q_row0 + q_lane) * p.Hq + hq) * (size_t)(D * 2);
 #pragma unroll
     for (int md = 0; md < MT2; ++md)
 #pragma unroll
@@ -652,7 +727,7 @@ fwd_kernel(FwdParams p) {
         *(u32x2*)(op + d * 2) = w;
       }
     if (hh == 0)
-      p.lse[((size_t)b * p.Hq + hq) * Nq + q_lane] = (m_run + __builtin_amdgcn_logf(lL)) * LN2;
+      p.lse[lse0 + q_lane] = empty ? -__builtin_inff() : (m_run + __builtin_amdgcn_logf(lL)) * LN2;
   }
 }
 

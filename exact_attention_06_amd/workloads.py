@@ -23,7 +23,8 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = ["Workload", "make_qkv", "sample_rows", "tiny", "ragged", "hd128_sweep",
-           "hd256_sweep", "video", "all_workloads", "by_name"]
+           "hd256_sweep", "video", "all_workloads", "by_name", "VarWorkload", "make_varlen",
+           "make_paged", "var_workloads", "var_inputs"]
 
 TOKENS = 32768  # batch is sized so that B * N is about this many tokens
 
@@ -127,3 +128,133 @@ def by_name(name):
 
 def inputs_for(w: Workload, dtype=torch.bfloat16):
     return make_qkv(w.B, w.N, w.N, w.Hq, w.Hkv, w.d, w.seed, dtype=dtype, k_spike=w.k_spike)
+
+
+# ---- variable-length batches and paged K/V caches (the serving variants: "[RFC] FA4 -
+#      head_dim=256 & head_dim=512", feature table of section "Phase 2"). Sequence lengths,
+#      page orders and values are seeded draws; nothing here computes attention.
+
+@dataclass(frozen=True)
+class VarWorkload:
+    name: str
+    seqlens_q: tuple       # query rows per sequence
+    seqlens_k: tuple       # keys per sequence (paged: seqused_k)
+    Hq: int
+    Hkv: int
+    d: int
+    seed: int
+    paged: bool = False
+    page_size: int = 128
+    causal_modes: tuple = (False, True)
+
+    @property
+    def B(self) -> int:
+        return len(self.seqlens_q)
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / self.d ** 0.5, dtype=torch.float32))
+
+    def flops(self, causal: bool) -> float:
+        """4*Hq*d per visible (query, key) pair; causal is aligned bottom-right."""
+        pairs = 0
+        for lq, lk in zip(self.seqlens_q, self.seqlens_k):
+            if not causal:
+                pairs += lq * lk
+            else:
+                # row i sees min(lk, max(0, i + 1 + lk - lq)) keys
+                for i in range(lq):
+                    pairs += min(lk, max(0, i + 1 + lk - lq))
+        return 4.0 * self.Hq * self.d * pairs
+
+
+def _lengths(n, lo, hi, seed):
+    """n lengths drawn log-uniformly in [lo, hi] (seeded)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    u = torch.rand(n, generator=g, dtype=torch.float64)
+    return tuple(int(x) for x in torch.exp(torch.log(torch.tensor(float(lo))) +
+                                            u * (torch.log(torch.tensor(float(hi))) -
+                                                 torch.log(torch.tensor(float(lo))))).round())
+
+
+def make_varlen(seqlens_q, seqlens_k, Hq, Hkv, d, seed, dtype=torch.bfloat16):
+    """Packed q [sum Lq, Hq, d], k and v [sum Lk, Hkv, d] (N(0,1) draws rounded to dtype)
+    and int32 offsets cu_seqlens_q, cu_seqlens_k (CPU tensors)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    tq, tk = int(sum(seqlens_q)), int(sum(seqlens_k))
+    q = torch.randn((tq, Hq, d), generator=g, dtype=torch.float32).to(dtype)
+    k = torch.randn((tk, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
+    v = torch.randn((tk, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
+    cu_q = torch.tensor([0] + list(torch.cumsum(torch.tensor(seqlens_q), 0).tolist()), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(torch.cumsum(torch.tensor(seqlens_k), 0).tolist()), dtype=torch.int32)
+    return q, k, v, cu_q, cu_k
+
+
+def make_paged(seqlens_q, seqused_k, page_size, Hq, Hkv, d, seed, dtype=torch.bfloat16, spare_pages=3):
+    """Packed q [sum Lq, Hq, d]; k_cache, v_cache [num_pages, page_size, Hkv, d] filled with
+    N(0,1) draws everywhere (rows past a sequence's keys hold unrelated values); a
+    block_table [B, max_pages] int32 that hands out the pages in a seeded random order
+    (unused entries point at page 0); int32 cu_seqlens_q and seqused_k. CPU tensors."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    B = len(seqlens_q)
+    need = [(n + page_size - 1) // page_size for n in seqused_k]
+    max_pages = max(1, max(need))
+    num_pages = sum(need) + spare_pages
+    q = torch.randn((int(sum(seqlens_q)), Hq, d), generator=g, dtype=torch.float32).to(dtype)
+    kc = torch.randn((num_pages, page_size, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
+    vc = torch.randn((num_pages, page_size, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
+    perm = torch.randperm(num_pages, generator=g)
+    bt = torch.zeros((B, max_pages), dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        for p in range(need[b]):
+            bt[b, p] = int(perm[nxt])
+            nxt += 1
+    cu_q = torch.tensor([0] + list(torch.cumsum(torch.tensor(seqlens_q), 0).tolist()), dtype=torch.int32)
+    used = torch.tensor(list(seqused_k), dtype=torch.int32)
+    return q, kc, vc, cu_q, used, bt
+
+
+def varlen_prefill():
+    """Packed prefill batch: 12 sequences of 64..4096 tokens (log-uniform), Lq == Lk,
+    hd128, 16 query heads over 4 KV heads."""
+    L = _lengths(12, 64, 4096, 31)
+    return VarWorkload("varlen_prefill_hd128", L, L, 16, 4, 128, 31)
+
+
+def chunked_prefill():
+    """Chunked prefill against a cache: 8 sequences, 512 new query rows each against
+    1024..8192 keys (bottom-right causal), hd128, 16 over 4 heads."""
+    Lk = _lengths(8, 1024, 8192, 32)
+    return VarWorkload("chunked_prefill_hd128", (512,) * 8, Lk, 16, 4, 128, 32, causal_modes=(True,))
+
+
+def paged_decode():
+    """Paged decode: 32 sequences with 1..16 new query rows (speculative decoding) against
+    256..16384 cached keys in 128-key pages, hd256, 8 query heads over 8 KV heads."""
+    Lk = _lengths(32, 256, 16384, 33)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(34)
+    Lq = tuple(int(x) for x in torch.randint(1, 17, (32,), generator=g))
+    return VarWorkload("paged_decode_hd256", Lq, Lk, 8, 8, 256, 33, paged=True, page_size=128,
+                       causal_modes=(True,))
+
+
+def paged_prefill():
+    """Paged prefill: 6 sequences of 128..4096 tokens (Lq == Lk) in 128-key pages, hd256,
+    8 query heads over 8 KV heads."""
+    L = _lengths(6, 128, 4096, 35)
+    return VarWorkload("paged_prefill_hd256", L, L, 8, 8, 256, 35, paged=True, page_size=128)
+
+
+def var_workloads():
+    return [varlen_prefill(), chunked_prefill(), paged_decode(), paged_prefill()]
+
+
+def var_inputs(w: VarWorkload, dtype=torch.bfloat16):
+    if w.paged:
+        return make_paged(w.seqlens_q, w.seqlens_k, w.page_size, w.Hq, w.Hkv, w.d, w.seed, dtype)
+    return make_varlen(w.seqlens_q, w.seqlens_k, w.Hq, w.Hkv, w.d, w.seed, dtype)

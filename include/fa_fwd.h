@@ -57,8 +57,11 @@ enum fa_status {
   FA_ERR_ALIGN = -6,        /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_TOO_LARGE = -7,    /* the work grid or a per-head extent exceeds 2^31 - 1         */
   FA_ERR_LAUNCH = -8,       /* the HIP launch reported an error                            */
-  FA_ERR_WORKSPACE = -9     /* backward: workspace NULL or smaller than
+  FA_ERR_WORKSPACE = -9,    /* backward: workspace NULL or smaller than
                                fa_bwd_workspace_bytes(B, Nq, Hq)                           */
+  FA_ERR_PAGE = -10         /* paged K/V: page_size not a positive multiple of 64, or
+                               num_pages / max_pages not positive, or a page extent
+                               (pages x page_size) above 2^31 - 1                          */
 };
 
 /* Forward pass, bf16 q/k/v/o, fp32 LSE. Arguments as described above; `scale` multiplies
@@ -71,6 +74,60 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
                void* stream);
+
+/* ---- Variable-length batches, per-sequence key counts and a paged K/V cache.
+ *
+ * The serving variants the pages list beside the dense pass ("[RFC] FA4 - head_dim=256 &
+ * head_dim=512", feature table of section "Phase 2": paged KV with the page size equal to
+ * the key tile, seqused_k with an early exit for sequences without keys, varlen; the Dutch
+ * page, section "Compatibiliteit en huidige status": variable-length batches through
+ * cu_seqlens). Each sequence b is computed exactly as the dense operation above, on its
+ * own rows, with these readings (the pages do not fix them):
+ *   - causal alignment is bottom-right: query i of a sequence with Lq queries and Lk keys
+ *     sees keys j <= i + (Lk - Lq) (the dense pass's mask when Lq == Lk; a decode row sees
+ *     every key); a query row that sees no key gets O = 0 and LSE = -inf;
+ *   - q and o are packed [total_q, Hq, d]; lse is [Hq, total_q] float32; sequence b owns
+ *     rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1;
+ *   - seqused_k[b] (when given) is the number of keys of sequence b that are used (the
+ *     first ones); 0 gives O = 0 and LSE = -inf for the whole sequence.
+ *
+ * cu_seqlens_q, cu_seqlens_k, seqused_k and block_table are int32 device arrays owned by
+ * the caller. Their contents are read on the GPU and are not validated on the host: offsets
+ * must be non-decreasing, cu_seqlens_q[B] <= total_q, every query length <= max_seqlen_q
+ * (rows beyond it are not written). Offsets are clamped to the tensors and page numbers
+ * outside [0, num_pages) read as zero pages, so bad contents give wrong numbers but no
+ * access outside the buffers. Everything else is as for fa_fwd (ownership, stream,
+ * error codes, alignment; the four int arrays must be 4-byte aligned).
+ */
+
+/* Packed K/V: k, v are [total_k, Hkv, d]; sequence b owns key rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 (B+1 entries). seqused_k: NULL or B entries. */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, const int* seqused_k,
+                  int B, int max_seqlen_q, int total_q, int total_k,
+                  int Hq, int Hkv, int d, int causal, float scale, void* stream);
+
+/* Same as fa_fwd_varlen with fp16 q/k/v/o. */
+int fa_fwd_varlen_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int* cu_seqlens_q, const int* cu_seqlens_k, const int* seqused_k,
+                      int B, int max_seqlen_q, int total_q, int total_k,
+                      int Hq, int Hkv, int d, int causal, float scale, void* stream);
+
+/* Paged K/V: k_cache, v_cache are [num_pages, page_size, Hkv, d]; block_table is
+ * [B, max_pages] int32; logical key t of sequence b is row t % page_size of page
+ * block_table[b * max_pages + t / page_size]; seqused_k (B entries, required) gives the
+ * key count of each sequence (at most max_pages * page_size). page_size is a multiple of
+ * 64, so a key tile never straddles two pages. */
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                 const int* cu_seqlens_q, const int* seqused_k, const int* block_table,
+                 int B, int max_seqlen_q, int total_q, int num_pages, int page_size, int max_pages,
+                 int Hq, int Hkv, int d, int causal, float scale, void* stream);
+
+/* Same as fa_fwd_paged with fp16 q/k/v/o. */
+int fa_fwd_paged_f16(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                     const int* cu_seqlens_q, const int* seqused_k, const int* block_table,
+                     int B, int max_seqlen_q, int total_q, int num_pages, int page_size,
+                     int max_pages, int Hq, int Hkv, int d, int causal, float scale, void* stream);
 
 /* Static, NUL-terminated description of an fa_status code (never NULL). */
 const char* fa_strerror(int code);

@@ -107,11 +107,15 @@ def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool, scal
 
 def gather_paged(cache, block_table, b: int, length: int) -> np.ndarray:
     """Logical rows 0..length-1 of sequence b from a paged cache [pages, page_size, H, d]."""
-    c = _f64(cache)
     bt = _ints(block_table)
-    page_size = c.shape[1]
+    page_size = cache.shape[1]
     t = np.arange(length)
-    return c[bt[b, t // page_size], t % page_size]
+    pages, rows = bt[b, t // page_size], t % page_size
+    if hasattr(cache, "detach"):  # torch tensor: gather first, then widen (exact)
+        import torch
+        return _f64(cache[torch.from_numpy(pages), torch.from_numpy(rows)])
+    c = np.asarray(cache)
+    return np.asarray(c[pages, rows], dtype=np.float64)
 
 
 def attention_paged_ref(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table, causal: bool,

@@ -34,7 +34,8 @@ def test_library_exports_every_header_symbol():
     lib = _lib.load()
     names = _lib.header_symbols()
     assert set(names) == {"fa_fwd", "fa_fwd_f16", "fa_strerror", "fa_fwd_check", "fa_bwd", "fa_bwd_f16",
-                          "fa_bwd_workspace_bytes"}
+                          "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_f16", "fa_fwd_paged",
+                          "fa_fwd_paged_f16"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -100,11 +101,11 @@ def test_entry_points_reject_before_any_hip_call(entry):
 
 def test_strerror_covers_codes():
     seen = set()
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         msg = _lib.strerror(code)
         assert msg and msg != "unknown fa status code"
         seen.add(msg)
-    assert len(seen) == 10
+    assert len(seen) == 11
     assert _lib.strerror(-99) == "unknown fa status code"
 
 
@@ -146,3 +147,63 @@ def test_bwd_rejects_before_any_hip_call(entry):
     assert _bwd(fn, ws=0) == _lib.FA_ERR_WORKSPACE
     assert _bwd(fn, wsb=4 * 2 * 300 * 8 - 4) == _lib.FA_ERR_WORKSPACE
     assert _bwd(fn, ws=A + 0x802) == _lib.FA_ERR_WORKSPACE
+
+
+# ---- variable-length and paged entry points: every rejection happens on the host
+
+VGOOD = dict(q=A, k=A + 0x100, v=A + 0x200, o=A + 0x300, lse=A + 0x400, cu_q=A + 0x500, cu_k=A + 0x600,
+             used=A + 0x700, bt=A + 0x800, B=3, max_q=64, total_q=100, total_k=200, num_pages=10,
+             page_size=128, max_pages=4, Hq=8, Hkv=2, d=128, causal=1, scale=0.0884)
+
+
+def _varlen(fn, **kw):
+    a = dict(VGOOD, **kw)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu_q"], a["cu_k"], a["used"], a["B"], a["max_q"],
+              a["total_q"], a["total_k"], a["Hq"], a["Hkv"], a["d"], a["causal"], ctypes.c_float(a["scale"]), None)
+
+
+def _paged(fn, **kw):
+    a = dict(VGOOD, **kw)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu_q"], a["used"], a["bt"], a["B"], a["max_q"],
+              a["total_q"], a["num_pages"], a["page_size"], a["max_pages"], a["Hq"], a["Hkv"], a["d"],
+              a["causal"], ctypes.c_float(a["scale"]), None)
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd_varlen", "fa_fwd_varlen_f16"])
+def test_varlen_rejects_before_any_hip_call(entry):
+    fn = getattr(_lib.load(), entry)
+    for f in ("q", "k", "v", "o", "lse", "cu_q", "cu_k"):
+        assert _varlen(fn, **{f: 0}) == _lib.FA_ERR_NULL, f
+    for kw in (dict(B=0), dict(max_q=0), dict(total_q=0), dict(total_k=-1), dict(Hq=0), dict(Hkv=3)):
+        assert _varlen(fn, **kw) == _lib.FA_ERR_SHAPE, kw
+    assert _varlen(fn, d=192) == _lib.FA_ERR_HEADDIM
+    assert _varlen(fn, scale=math.inf) == _lib.FA_ERR_SCALE
+    for kw in (dict(q=A + 8), dict(o=A + 4), dict(lse=A + 2), dict(cu_q=A + 1), dict(cu_k=A + 2),
+               dict(used=A + 3)):
+        assert _varlen(fn, **kw) == _lib.FA_ERR_ALIGN, kw
+    assert _varlen(fn, B=1 << 20, Hq=1 << 10, Hkv=1 << 10, max_q=1 << 12) == _lib.FA_ERR_TOO_LARGE
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd_paged", "fa_fwd_paged_f16"])
+def test_paged_rejects_before_any_hip_call(entry):
+    fn = getattr(_lib.load(), entry)
+    for f in ("q", "k", "v", "o", "lse", "cu_q", "used", "bt"):
+        assert _paged(fn, **{f: 0}) == _lib.FA_ERR_NULL, f
+    for kw in (dict(B=0), dict(max_q=0), dict(total_q=0), dict(Hq=4, Hkv=8)):
+        assert _paged(fn, **kw) == _lib.FA_ERR_SHAPE, kw
+    for kw in (dict(page_size=0), dict(page_size=96), dict(page_size=-128), dict(num_pages=0),
+               dict(max_pages=0), dict(max_pages=1 << 24), dict(num_pages=1 << 24)):
+        assert _paged(fn, **kw) == _lib.FA_ERR_PAGE, kw
+    assert _paged(fn, d=64) == _lib.FA_ERR_HEADDIM
+    assert _paged(fn, scale=-1.0) == _lib.FA_ERR_SCALE
+    for kw in (dict(k=A + 8), dict(bt=A + 2), dict(used=A + 1)):
+        assert _paged(fn, **kw) == _lib.FA_ERR_ALIGN, kw
+
+
+def test_varlen_python_layer_rejects_cpu_tensors():
+    q = torch.zeros(10, 2, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward_varlen(q, q, q, cu, cu, 10)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward_paged(q, q[None], q[None], cu, cu[1:], cu[None], 10)

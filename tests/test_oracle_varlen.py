@@ -177,8 +177,8 @@ MUTANTS = {
     "top_left_alignment": ("(j <= i + (lk - lq))", "(j <= i)"),
     "mask_includes_next_key": ("(j <= i + (lk - lq))", "(j <= i + 1 + (lk - lq))"),
     "seqused_ignored": ("k1 = k0 + min(int(used[b]), k1 - k0)", "k1 = k1"),
-    "page_row_and_page_swapped": ("return c[bt[b, t // page_size], t % page_size]",
-                                  "return c[bt[b, t % page_size], t // page_size]"),
+    "page_row_and_page_swapped": ("pages, rows = bt[b, t // page_size], t % page_size",
+                                  "pages, rows = bt[b, t % page_size], t // page_size"),
     "empty_rows_lse_zero": ("lse[h] = np.where(any_visible, m[:, 0] + np.log(safe[:, 0]), -np.inf)",
                             "lse[h] = np.where(any_visible, m[:, 0] + np.log(safe[:, 0]), 0.0)"),
     "gqa_modulo": ("kvh = h // group", "kvh = h % hkv"),
