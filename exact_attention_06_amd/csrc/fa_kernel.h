@@ -128,15 +128,19 @@ __device__ __forceinline__ float other_half(float x) {
 }
 
 // Block id -> (b*Hq + h, query tile). Workgroups are dispatched round-robin over the 8
-// XCDs (bid % 8); when B*Hq is a multiple of 8, each XCD gets a contiguous set of heads so
-// that workgroups sharing K/V run on the same XCD and share its L2. Causal work is ordered
-// longest-first (highest query tile first) inside each XCD's share.
-template <bool CAUSAL>
+// XCDs (bid % 8). Dense batches (all heads carry equal work): when B*Hq is a multiple of 8,
+// each XCD gets a contiguous set of heads, so the query heads of a GQA group and all query
+// tiles of a head share one XCD's L2 for their K/V. Variable-length batches (SPREAD): head
+// bh = bid % (B*Hq), so the heads of one sequence go to different XCDs (a long sequence
+// would otherwise occupy one XCD only) while each head keeps one XCD when B*Hq % 8 == 0.
+// LONGEST_FIRST (causal, and every variable-length batch, where a high query tile exists
+// only in long sequences): highest query tile first.
+template <bool LONGEST_FIRST, bool SPREAD>
 __device__ __forceinline__ void decode_block(int bid, const FwdParams& p, int& bh, int& qt) {
   const int BH = p.B * p.Hq;
-  if ((BH & 7) == 0) {
+  if (!SPREAD && (BH & 7) == 0) {
     const int xcd = bid & 7, slot = bid >> 3, hpx = BH >> 3;
-    if (CAUSAL) {
+    if (LONGEST_FIRST) {
       qt = p.nqt - 1 - slot / hpx;
       bh = xcd * hpx + slot % hpx;
     } else {
@@ -144,7 +148,7 @@ __device__ __forceinline__ void decode_block(int bid, const FwdParams& p, int& b
       qt = slot % p.nqt;
     }
   } else {
-    if (CAUSAL) {
+    if (LONGEST_FIRST) {
       qt = p.nqt - 1 - bid / BH;
       bh = bid % BH;
     } else {
@@ -220,7 +224,7 @@ fwd_kernel(FwdParams p) {
   const int hh = lane >> 5;
 
   int bh, qt;
-  decode_block<CAUSAL>(blockIdx.x, p, bh, qt);
+  decode_block<CAUSAL || VAR, VAR>(blockIdx.x, p, bh, qt);
   const int b = bh / p.Hq;
   const int hq = bh - b * p.Hq;
   const int kvh = hq / p.group;

@@ -178,34 +178,40 @@ def _lengths(n, lo, hi, seed):
                                                  torch.log(torch.tensor(float(lo))))).round())
 
 
-def make_varlen(seqlens_q, seqlens_k, Hq, Hkv, d, seed, dtype=torch.bfloat16):
+def make_varlen(seqlens_q, seqlens_k, Hq, Hkv, d, seed, dtype=torch.bfloat16, device="cpu"):
     """Packed q [sum Lq, Hq, d], k and v [sum Lk, Hkv, d] (N(0,1) draws rounded to dtype)
-    and int32 offsets cu_seqlens_q, cu_seqlens_k (CPU tensors)."""
-    g = torch.Generator(device="cpu")
+    and int32 offsets cu_seqlens_q, cu_seqlens_k (CPU tensors). device="cuda" draws the
+    values on the GPU (other numbers, same distribution: for timing only)."""
+    g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     tq, tk = int(sum(seqlens_q)), int(sum(seqlens_k))
-    q = torch.randn((tq, Hq, d), generator=g, dtype=torch.float32).to(dtype)
-    k = torch.randn((tk, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
-    v = torch.randn((tk, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
+    q = torch.randn((tq, Hq, d), generator=g, dtype=torch.float32, device=device).to(dtype)
+    k = torch.randn((tk, Hkv, d), generator=g, dtype=torch.float32, device=device).to(dtype)
+    v = torch.randn((tk, Hkv, d), generator=g, dtype=torch.float32, device=device).to(dtype)
     cu_q = torch.tensor([0] + list(torch.cumsum(torch.tensor(seqlens_q), 0).tolist()), dtype=torch.int32)
     cu_k = torch.tensor([0] + list(torch.cumsum(torch.tensor(seqlens_k), 0).tolist()), dtype=torch.int32)
     return q, k, v, cu_q, cu_k
 
 
-def make_paged(seqlens_q, seqused_k, page_size, Hq, Hkv, d, seed, dtype=torch.bfloat16, spare_pages=3):
+def make_paged(seqlens_q, seqused_k, page_size, Hq, Hkv, d, seed, dtype=torch.bfloat16, spare_pages=3,
+               device="cpu"):
     """Packed q [sum Lq, Hq, d]; k_cache, v_cache [num_pages, page_size, Hkv, d] filled with
     N(0,1) draws everywhere (rows past a sequence's keys hold unrelated values); a
     block_table [B, max_pages] int32 that hands out the pages in a seeded random order
-    (unused entries point at page 0); int32 cu_seqlens_q and seqused_k. CPU tensors."""
+    (unused entries point at page 0); int32 cu_seqlens_q and seqused_k. CPU tensors
+    (device="cuda": q and the caches are drawn on the GPU, for timing only)."""
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
+    gv = g if device == "cpu" else torch.Generator(device=device)
+    if device != "cpu":
+        gv.manual_seed(int(seed))
     B = len(seqlens_q)
     need = [(n + page_size - 1) // page_size for n in seqused_k]
     max_pages = max(1, max(need))
     num_pages = sum(need) + spare_pages
-    q = torch.randn((int(sum(seqlens_q)), Hq, d), generator=g, dtype=torch.float32).to(dtype)
-    kc = torch.randn((num_pages, page_size, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
-    vc = torch.randn((num_pages, page_size, Hkv, d), generator=g, dtype=torch.float32).to(dtype)
+    q = torch.randn((int(sum(seqlens_q)), Hq, d), generator=gv, dtype=torch.float32, device=device).to(dtype)
+    kc = torch.randn((num_pages, page_size, Hkv, d), generator=gv, dtype=torch.float32, device=device).to(dtype)
+    vc = torch.randn((num_pages, page_size, Hkv, d), generator=gv, dtype=torch.float32, device=device).to(dtype)
     perm = torch.randperm(num_pages, generator=g)
     bt = torch.zeros((B, max_pages), dtype=torch.int32)
     nxt = 0
@@ -254,7 +260,34 @@ def var_workloads():
     return [varlen_prefill(), chunked_prefill(), paged_decode(), paged_prefill()]
 
 
-def var_inputs(w: VarWorkload, dtype=torch.bfloat16):
+def var_inputs(w: VarWorkload, dtype=torch.bfloat16, device="cpu"):
     if w.paged:
-        return make_paged(w.seqlens_q, w.seqlens_k, w.page_size, w.Hq, w.Hkv, w.d, w.seed, dtype)
-    return make_varlen(w.seqlens_q, w.seqlens_k, w.Hq, w.Hkv, w.d, w.seed, dtype)
+        return make_paged(w.seqlens_q, w.seqlens_k, w.page_size, w.Hq, w.Hkv, w.d, w.seed, dtype, device=device)
+    return make_varlen(w.seqlens_q, w.seqlens_k, w.Hq, w.Hkv, w.d, w.seed, dtype, device=device)
+
+
+def _lengths_to_total(total, lo, hi, seed):
+    """Log-uniform lengths in [lo, hi] (seeded) until they sum to at least `total`; the last
+    one is cut so that the sum is exactly `total`."""
+    out, s, k = [], 0, 0
+    while s < total:
+        n = _lengths(1, lo, hi, seed * 1000 + k)[0]
+        n = min(n, total - s)
+        out.append(n)
+        s += n
+        k += 1
+    return tuple(out)
+
+
+def bench_var_workloads():
+    """Throughput-size serving batches (about 32k query tokens for prefill)."""
+    L1 = _lengths_to_total(32768, 256, 8192, 61)
+    L2 = _lengths_to_total(32768, 256, 8192, 62)
+    Lk = _lengths(128, 1024, 32768, 63)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(64)
+    Lq = tuple(int(x) for x in torch.randint(1, 17, (128,), generator=g))
+    return [VarWorkload("varlen_prefill_32k_hd128", L1, L1, 16, 4, 128, 61),
+            VarWorkload("paged_prefill_32k_hd256", L2, L2, 8, 8, 256, 62, paged=True, page_size=128),
+            VarWorkload("paged_decode_128seq_hd256", Lq, Lk, 8, 8, 256, 63, paged=True, page_size=128,
+                        causal_modes=(True,))]
