@@ -252,6 +252,41 @@ def main():
             del qx, kx, vx, dox, o, lse
             torch.cuda.empty_cache()
 
+    # short sequences, few heads: the plain grid vs split-KV (the library's split count)
+    short = []
+    if not args.no_sweep:
+        for (B_, N_, H_, d_) in ((1, 1024, 8, 256), (2, 1024, 8, 256), (1, 2048, 8, 256), (1, 1024, 16, 128)):
+            g = torch.Generator(device="cuda")
+            g.manual_seed(71)
+            qx = torch.randn((B_, N_, H_, d_), generator=g, device="cuda").to(torch.bfloat16)
+            kx = torch.randn((B_, N_, H_, d_), generator=g, device="cuda").to(torch.bfloat16)
+            vx = torch.randn((B_, N_, H_, d_), generator=g, device="cuda").to(torch.bfloat16)
+            for c in (False, True):
+                fl = 4.0 * B_ * H_ * N_ * N_ * d_ / (2 if c else 1)
+                ns = fa.num_splits(B_, N_, N_, H_, d_, c)
+                res = {}
+                for mode, fn in (("plain", lambda: fa.forward(qx, kx, vx, causal=c)),
+                                 ("splitkv", lambda: fa.forward_splitkv(qx, kx, vx, causal=c, num_splits=ns))):
+                    for _ in range(3):
+                        fn()
+                    torch.cuda.synchronize()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    n = 20
+                    e0.record()
+                    for _ in range(n):
+                        fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    res[mode] = e0.elapsed_time(e1) / n
+                ent = {"B": B_, "N": N_, "Hq": H_, "d": d_, "causal": c, "splits": ns,
+                       "plain_ms": round(res["plain"], 4), "splitkv_ms": round(res["splitkv"], 4),
+                       "plain_tflops": round(fl / (res["plain"] * 1e-3) / 1e12, 1),
+                       "splitkv_tflops": round(fl / (res["splitkv"] * 1e-3) / 1e12, 1)}
+                short.append(ent)
+                log(f"[short] B={B_} N={N_} Hq={H_} d={d_} {'causal' if c else 'noncausal':9s} plain "
+                    f"{ent['plain_tflops']:7.1f} TFLOPS, split-KV x{ns} {ent['splitkv_tflops']:7.1f} TFLOPS")
+
     # serving variants: packed variable-length prefill, paged prefill, paged decode
     variants = []
     if not args.no_sweep:
@@ -318,6 +353,7 @@ def main():
         "sweep": sweep,
         "backward": backward,
         "variants": variants,
+        "short_splitkv": short,
         "kernel_source_hash": kernel_source_hash(),
     }
     if b200:

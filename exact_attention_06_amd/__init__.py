@@ -2,6 +2,7 @@
 
     o, lse = forward(q, k, v, causal=False, scale=None)
     dq, dk, dv = backward(q, k, v, o, lse, dout, causal=False, scale=None)
+    o, lse = forward_splitkv(q, k, v, causal=False, scale=None, num_splits=None)
     o, lse = forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False,
                             scale=None, seqused_k=None)
     o, lse = forward_paged(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
@@ -22,7 +23,8 @@ import math
 
 from . import _lib
 
-__all__ = ["forward", "backward", "forward_varlen", "forward_paged", "check_args", "FaError"]
+__all__ = ["forward", "forward_splitkv", "num_splits", "backward", "forward_varlen", "forward_paged",
+           "check_args", "FaError"]
 
 
 class FaError(ValueError):
@@ -85,6 +87,51 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), float(scale), stream)
+    if rc != 0:
+        _raise(rc)
+    return out, lse
+
+
+def num_splits(B, Nq, Nk, Hq, d, causal=False) -> int:
+    """The library's split count for a shape (fa_fwd_num_splits; 1 = no split)."""
+    return int(_lib.load().fa_fwd_num_splits(B, Nq, Nk, Hq, d, int(bool(causal))))
+
+
+def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_splits=None):
+    """forward() with the key range of every query tile split over num_splits workgroups
+    (fa_fwd_splitkv); num_splits=None takes the library's choice. The workspace is
+    allocated here with torch."""
+    import torch
+
+    lib = _lib.load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [batch, seq, heads, head_dim]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    if q.dtype == torch.bfloat16:
+        fn = lib.fa_fwd_splitkv
+    elif q.dtype == torch.float16:
+        fn = lib.fa_fwd_splitkv_f16
+    else:
+        raise ValueError("dtype must be bfloat16 or float16")
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q/k/v shapes do not match: q [B,Nq,Hq,d], k and v [B,Nk,Hkv,d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        num_splits = int(lib.fa_fwd_num_splits(B, Nq, Nk, Hq, d, int(bool(causal))))
+    nbytes = int(lib.fa_fwd_splitkv_workspace_bytes(B, Nq, Hq, d, int(num_splits)))
+    ws = torch.empty(max(4, nbytes // 4), dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), ws.data_ptr(), nbytes,
+                B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), float(scale), int(num_splits), stream)
     if rc != 0:
         _raise(rc)
     return out, lse

@@ -37,6 +37,8 @@ _VARLEN_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, 
 # q, kc, vc, o, lse, cu_q, seqused, block_table, B, max_seqlen_q, total_q, num_pages, page_size,
 # max_pages, Hq, Hkv, d, causal, scale, stream
 _PAGED_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+# q, k, v, o, lse, workspace, workspace_bytes, B, Nq, Nk, Hq, Hkv, d, causal, scale, num_splits, stream
+_SPLIT_ARGS = [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P]
 _BWD_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _I, _I, _I,
              ctypes.c_float, _P]
 
@@ -58,6 +60,14 @@ def load():
                 fn = getattr(lib, name)
                 fn.argtypes = args
                 fn.restype = _I
+        for name in ("fa_fwd_splitkv", "fa_fwd_splitkv_f16"):
+            fn = getattr(lib, name)
+            fn.argtypes = _SPLIT_ARGS
+            fn.restype = _I
+        lib.fa_fwd_splitkv_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+        lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_num_splits.argtypes = [_I, _I, _I, _I, _I, _I]
+        lib.fa_fwd_num_splits.restype = _I
         for name in ("fa_bwd", "fa_bwd_f16"):
             fn = getattr(lib, name)
             fn.argtypes = _BWD_ARGS

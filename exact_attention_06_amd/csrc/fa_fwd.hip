@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <algorithm>
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
@@ -14,12 +15,18 @@
 
 namespace {
 
-template <int D, bool CAUSAL, class T, bool VAR>
+template <int D, bool CAUSAL, class T, int VM>
 int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
   using L = fa::Layout<D>;
   // the kernel's K/V buffers are static LDS (L::LDS bytes, within gfx950's 160 KB per CU)
-  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, T, VAR>), dim3(grid), dim3(L::NW * 64), 0, stream, prm);
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, T, VM>), dim3(grid), dim3(L::NW * 64), 0, stream, prm);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  if (VM == 2) {  // split-KV: merge the partials
+    const size_t threads = (size_t)prm.B * prm.Hq * prm.Nq * (D / 8);
+    hipLaunchKernelGGL((fa::fwd_combine<D, T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, prm);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  }
+  return FA_OK;
 }
 
 // Scale: a zero (or subnormal) scale makes every visible score exactly 0; the kernel then
@@ -29,14 +36,21 @@ void set_scale(fa::FwdParams& prm, float scale) {
   prm.c = prm.zero_scores ? fa::LOG2E : scale * fa::LOG2E;
 }
 
-template <bool VAR, class T>
+template <int VM, class T>
 int dispatch(fa::FwdParams& prm, int d, int causal, hipStream_t s) {
   const int BR = d == 128 ? fa::Layout<128>::BR : fa::Layout<256>::BR;
   prm.nqt = (prm.Nq + BR - 1) / BR;
-  const int grid = prm.B * prm.Hq * prm.nqt;
+  const int grid = prm.B * prm.Hq * prm.nqt * (VM == 2 ? prm.splits : 1);
   if (d == 128)
-    return causal ? launch<128, true, T, VAR>(prm, grid, s) : launch<128, false, T, VAR>(prm, grid, s);
-  return causal ? launch<256, true, T, VAR>(prm, grid, s) : launch<256, false, T, VAR>(prm, grid, s);
+    return causal ? launch<128, true, T, VM>(prm, grid, s) : launch<128, false, T, VM>(prm, grid, s);
+  return causal ? launch<256, true, T, VM>(prm, grid, s) : launch<256, false, T, VM>(prm, grid, s);
+}
+
+void clear_extras(fa::FwdParams& prm) {
+  prm.cu_q = prm.cu_k = prm.seqused = prm.block_table = nullptr;
+  prm.total_q = prm.total_k = prm.page_size = prm.max_pages = prm.num_pages = 0;
+  prm.part_o = prm.part_lse = nullptr;
+  prm.splits = prm.tps = 0;
 }
 
 template <int D> int br() { return fa::Layout<D>::BR; }
@@ -74,10 +88,70 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   prm.Hq = Hq;
   prm.Hkv = Hkv;
   prm.group = Hq / Hkv;
-  prm.cu_q = prm.cu_k = prm.seqused = prm.block_table = nullptr;
-  prm.total_q = prm.total_k = prm.page_size = prm.max_pages = prm.num_pages = 0;
+  clear_extras(prm);
   set_scale(prm, scale);
-  return dispatch<false, T>(prm, d, causal, (hipStream_t)stream);
+  return dispatch<0, T>(prm, d, causal, (hipStream_t)stream);
+}
+
+// ---- split-KV forward: the key tiles of each query tile are cut into num_splits ranges
+int key_tile(int d) { return d == 128 ? fa::Layout<128>::BC : fa::Layout<256>::BC; }
+
+size_t splitkv_ws_bytes(int B, int Nq, int Hq, int d, int splits) {
+  if (B <= 0 || Nq <= 0 || Hq <= 0 || (d != 128 && d != 256) || splits < 1) return 0;
+  return (size_t)splits * B * Hq * Nq * (size_t)(d + 1) * sizeof(float);
+}
+
+// Split count from measurements on MI355X (hd128 and hd256, 1..4 batches of 1k..8k tokens,
+// 8 or 16 heads): splitting pays while the plain grid has at most ~256 workgroups, more so
+// for causal shapes and long key ranges; beyond that the partials' workspace traffic costs
+// more than the extra parallelism brings. At least 4 key tiles per split.
+int num_splits(int B, int Nq, int Nk, int Hq, int d, int causal) {
+  if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || (d != 128 && d != 256)) return 1;
+  const int BR = d == 128 ? fa::Layout<128>::BR : fa::Layout<256>::BR;
+  const int64_t blocks = (int64_t)B * Hq * ((Nq + BR - 1) / BR);
+  const int ntiles = (Nk + key_tile(d) - 1) / key_tile(d);
+  int s = 1;
+  if (blocks <= 64)
+    s = 4;
+  else if (blocks <= 160)
+    s = 2;
+  else if (blocks <= 256 && Nk >= 4096)
+    s = causal ? 3 : 2;
+  else if (blocks <= 512 && Nk >= 8192 && causal)
+    s = 2;
+  return std::max(1, std::min(s, ntiles / 4));
+}
+
+template <class T>
+int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale, int splits,
+                void* stream) {
+  const int st = check(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale);
+  if (st != FA_OK) return st;
+  if (splits < 1 || splits > 256) return FA_ERR_SHAPE;
+  const size_t need = splitkv_ws_bytes(B, Nq, Hq, d, splits);
+  if (!ws || ws_bytes < need || ((uintptr_t)ws & 15)) return FA_ERR_WORKSPACE;
+  if ((int64_t)B * Hq * ((Nq + 127) / 128) * splits > INT_MAX) return FA_ERR_TOO_LARGE;
+  fa::FwdParams prm;
+  prm.q = (const uint8_t*)q;
+  prm.k = (const uint8_t*)k;
+  prm.v = (const uint8_t*)v;
+  prm.o = (uint8_t*)o;
+  prm.lse = lse;
+  prm.B = B;
+  prm.Nq = Nq;
+  prm.Nk = Nk;
+  prm.Hq = Hq;
+  prm.Hkv = Hkv;
+  prm.group = Hq / Hkv;
+  clear_extras(prm);
+  const int ntiles = (Nk + key_tile(d) - 1) / key_tile(d);
+  prm.tps = (ntiles + splits - 1) / splits;
+  prm.splits = splits;
+  prm.part_o = (float*)ws;
+  prm.part_lse = (float*)ws + (size_t)splits * B * Hq * Nq * d;
+  set_scale(prm, scale);
+  return dispatch<2, T>(prm, d, causal, (hipStream_t)stream);
 }
 
 // Variable-length forward (packed K/V when block_table is NULL, else paged K/V).
@@ -134,8 +208,10 @@ int run_var(const void* q, const void* k, const void* v, void* o, float* lse, co
   prm.page_size = paged ? page_size : 0;
   prm.max_pages = paged ? max_pages : 0;
   prm.num_pages = paged ? num_pages : 0;
+  prm.part_o = prm.part_lse = nullptr;
+  prm.splits = prm.tps = 0;
   set_scale(prm, scale);
-  return dispatch<true, T>(prm, d, causal, (hipStream_t)stream);
+  return dispatch<1, T>(prm, d, causal, (hipStream_t)stream);
 }
 
 size_t bwd_ws_bytes(int B, int Nq, int Hq) {
@@ -247,6 +323,28 @@ int fa_fwd_paged_f16(const void* q, const void* k_cache, const void* v_cache, vo
                           stream, true);
 }
 
+size_t fa_fwd_splitkv_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits) {
+  return splitkv_ws_bytes(B, Nq, Hq, d, num_splits);
+}
+
+int fa_fwd_num_splits(int B, int Nq, int Nk, int Hq, int d, int causal) {
+  return num_splits(B, Nq, Nk, Hq, d, causal);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                   size_t workspace_bytes, int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
+                   int num_splits, void* stream) {
+  return run_splitkv<fa::Bf16>(q, k, v, o, lse, workspace, workspace_bytes, B, Nq, Nk, Hq, Hkv, d, causal, scale,
+                               num_splits, stream);
+}
+
+int fa_fwd_splitkv_f16(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                       size_t workspace_bytes, int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal,
+                       float scale, int num_splits, void* stream) {
+  return run_splitkv<fa::F16>(q, k, v, o, lse, workspace, workspace_bytes, B, Nq, Nk, Hq, Hkv, d, causal, scale,
+                              num_splits, stream);
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Nq, int Hq) { return bwd_ws_bytes(B, Nq, Hq); }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -274,7 +372,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_TOO_LARGE: return "problem too large for 32-bit grid or sequence indexing";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
-    case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or smaller than fa_bwd_workspace_bytes";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than the *_workspace_bytes size";
     case FA_ERR_PAGE: return "paged K/V: page_size must be a positive multiple of 64, num_pages and max_pages positive";
     default: return "unknown fa status code";
   }

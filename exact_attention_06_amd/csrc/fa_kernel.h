@@ -42,6 +42,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
@@ -114,6 +115,13 @@ struct FwdParams {
   const int* block_table;
   int total_q, total_k;
   int page_size, max_pages, num_pages;
+  // split-KV (kernel variant SPLITK): the key tiles of every query tile are cut into `splits`
+  // ranges of `tps` tiles; block (split s, head, query tile) writes its normalised partial
+  // output to part_o [splits, B*Hq, Nq, D] and its log-sum-exp to part_lse [splits, B*Hq, Nq]
+  // (fp32), which fwd_combine merges.
+  float* part_o;
+  float* part_lse;
+  int splits, tps;
 };
 
 template <bool V> struct BoolC { static constexpr bool value = V; };
@@ -195,9 +203,12 @@ struct Layout {
   static constexpr int LDS = 2 * KBUF + 2 * VBUF;  // two K and two V buffers
 };
 
-template <int D, bool CAUSAL, class T, bool VAR>
+// VM: 0 dense batch, 1 variable-length batch (packed or paged K/V), 2 dense batch with the
+// key range of each query tile split over several blocks (split-KV).
+template <int D, bool CAUSAL, class T, int VM>
 __global__ void __launch_bounds__(TileCfg<D>::NW * 64, TileCfg<D>::WPE)
 fwd_kernel(FwdParams p) {
+  constexpr bool VAR = VM == 1, SPLITK = VM == 2;
   using x8 = typename T::x8;
   using x2 = typename T::x2;
   using L = Layout<D>;
@@ -223,8 +234,15 @@ fwd_kernel(FwdParams p) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  int bh, qt;
-  decode_block<CAUSAL || VAR, VAR>(blockIdx.x, p, bh, qt);
+  int bh, qt, split = 0;
+  if constexpr (SPLITK) {
+    // all blocks of split 0 first, then split 1, ...; within a split the dense order
+    const int per = p.B * p.Hq * p.nqt;
+    split = blockIdx.x / per;
+    decode_block<CAUSAL, false>(blockIdx.x - split * per, p, bh, qt);
+  } else {
+    decode_block<CAUSAL || VAR, VAR>(blockIdx.x, p, bh, qt);
+  }
   const int b = bh / p.Hq;
   const int hq = bh - b * p.Hq;
   const int kvh = hq / p.group;
@@ -274,11 +292,34 @@ fwd_kernel(FwdParams p) {
 
   int kend = Nk;
   if (CAUSAL) kend = min(Nk, min(Nq, q_wg0 + BR) + cshift);
-  const int ntiles = (kend + BC - 1) / BC;
-  // tiles this wave computes on (causal: keys up to its last query). Dense: at least tile 0;
-  // VAR: a wave whose rows see no key at all has none.
-  const int wtiles = CAUSAL ? max(VAR ? 0 : 1, min(ntiles, (min(qw0 + 32, Nq) + cshift + BC - 1) / BC))
-                            : ntiles;
+  // Key tiles t0 .. t0 + ntiles - 1 are this block's (split-KV: one range of tps tiles; else
+  // all). Loop indices below are relative to t0. Tiles below nfull are visible to every query
+  // of the block; a wave computes on its first wtiles tiles (causal: keys up to its last
+  // query; a wave whose rows see no key of the range has none).
+  const int ntiles_all = (kend + BC - 1) / BC;
+  const int wtiles_all =
+      CAUSAL ? max(VAR || SPLITK ? 0 : 1, min(ntiles_all, (min(qw0 + 32, Nq) + cshift + BC - 1) / BC))
+             : ntiles_all;
+  int nfull_all = Nk / BC;
+  if (CAUSAL) nfull_all = max(0, min(nfull_all, (q_wg0 + 1 + cshift) / BC));
+  const int t0 = SPLITK ? split * p.tps : 0;
+  const int t1 = SPLITK ? min(ntiles_all, t0 + p.tps) : ntiles_all;
+  const int ntiles = max(0, t1 - t0);
+  const int wtiles = max(0, min(wtiles_all, t1) - t0);
+  const int nfull = max(0, min(nfull_all, t1) - t0);
+  const int kfirst = t0 * BC;  // first key of the range
+  if (SPLITK && ntiles == 0) {  // a split past the keys of this query tile: empty partial
+    if (q_lane < Nq) {
+      const size_t row = ((size_t)split * p.B * p.Hq + bh) * Nq + q_lane;
+      float* po = p.part_o + row * D;
+#pragma unroll
+      for (int md = 0; md < MT2; ++md)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(f32x4*)(po + 32 * md + 8 * i + 4 * hh) = f32x4{};
+      if (hh == 0) p.part_lse[row] = -__builtin_inff();
+    }
+    return;
+  }
   if (VAR && kend <= 0) {  // no row of this block sees a key: O = 0, LSE = -inf
     if (q_lane < Nq) {
       uint8_t* op = p.o + ((q_row0 + q_lane) * p.Hq + hq) * (size_t)(D * 2);
@@ -341,7 +382,7 @@ fwd_kernel(FwdParams p) {
   auto load_tile = [&](int tile, const uint8_t* gbase, uint8_t* ldst, const uint32_t* vo,
                        auto nw_tag) {
     constexpr int NPW = decltype(nw_tag)::value;
-    const int k0 = tile * BC;
+    const int k0 = (t0 + tile) * BC;
     const uint8_t* tbase = gbase + (size_t)k0 * kv_row;
     int rows = min(BC, Nk - k0);
     if constexpr (VAR) {
@@ -418,7 +459,7 @@ fwd_kernel(FwdParams p) {
   // tile mt holds key k0 + 32mt + 8(r/4) + 4hh + r%4 for the lane's query q_lane, so a key
   // is visible iff its compile-time offset 32mt + 8(r/4) + r%4 is <= one per-lane limit.
   auto mask = [&](int j, f32x16 (&s)[MT1]) {
-    const int k0 = j * BC;
+    const int k0 = (t0 + j) * BC;
     const bool need = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > qw0 + cshift));
     if (need) {
       const int last = CAUSAL ? min(q_lane + cshift, Nk - 1) : Nk - 1;  // last visible key
@@ -483,9 +524,6 @@ fwd_kernel(FwdParams p) {
     lL += sumL;
     lO += sumO;
   };
-
-  int nfull = Nk / BC;
-  if (CAUSAL) nfull = max(0, min(nfull, (q_wg0 + 1 + cshift) / BC));
 
   if constexpr (TileCfg<D>::MODE == SEQ) {
   // ---- sequential tile loop. Iteration j: loads of K(j+1), V(j+1) in flight; S = Q K(j)^T;
@@ -709,14 +747,30 @@ fwd_kernel(FwdParams p) {
   lL += other_half(lL);
   lO += other_half(lO);
   if (q_lane < Nq) {
-    // VAR, causal: a row that sees no key (q_lane + cshift < 0) stores O = 0, LSE = -inf
-    const bool empty = VAR && CAUSAL && q_lane + cshift < 0;
+    // causal: a row that sees no key of this block's range (VAR: q_lane + cshift < 0; split-KV:
+    // a range that starts past the row's last key) stores O = 0, LSE = -inf
+    const bool empty = (VAR || SPLITK) && CAUSAL && q_lane + cshift < kfirst;
     if (empty) {
       lO = 1.f;
 #pragma unroll
       for (int md = 0; md < MT2; ++md) acc[md] = f32x16{};
     }
     const float inv = 1.0f / lO;
+    if constexpr (SPLITK) {  // normalised fp32 partial and its log-sum-exp
+      const size_t row = ((size_t)split * p.B * p.Hq + bh) * Nq + q_lane;
+      float* po = p.part_o + row * D;
+#pragma unroll
+      for (int md = 0; md < MT2; ++md)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 w;
+          for (int e = 0; e < 4; ++e) w[e] = acc[md][4 * i + e] * inv;
+          *(f32x4*)(po + 32 * md + 8 * i + 4 * hh) = w;
+        }
+      if (hh == 0)
+        p.part_lse[row] = empty ? -__builtin_inff() : (m_run + __builtin_amdgcn_logf(lL)) * LN2;
+      return;
+    }
     uint8_t* op = p.o + ((q_row0 + q_lane) * p.Hq + hq) * (size_t)(D * 2);
 #pragma unroll
     for (int md = 0; md < MT2; ++md)
@@ -733,6 +787,48 @@ fwd_kernel(FwdParams p) {
     if (hh == 0)
       p.lse[lse0 + q_lane] = empty ? -__builtin_inff() : (m_run + __builtin_amdgcn_logf(lL)) * LN2;
   }
+}
+
+// Merge of the split-KV partials (exact): for each row, LSE = ln sum_s exp(LSE_s) and
+// O = sum_s exp(LSE_s - LSE) * O_s, where O_s is split s's normalised output. A split that
+// saw no key of the row has LSE_s = -inf and weight 0. One thread per (row, 8 head-dim
+// values); the result goes to o [B, Nq, Hq, D] (T) and lse [B, Hq, Nq].
+template <int D, class T>
+__global__ void __launch_bounds__(256) fwd_combine(FwdParams p) {
+  using x2 = typename T::x2;
+  constexpr int G = D / 8;
+  const size_t rows = (size_t)p.B * p.Hq * p.Nq;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * G) return;
+  const size_t r = idx / G;  // (b*Hq + h) * Nq + i
+  const int g = (int)(idx - r * G);
+  const size_t plane = rows;  // rows per split
+  float m = -__builtin_inff();
+  for (int s = 0; s < p.splits; ++s) m = __builtin_fmaxf(m, p.part_lse[s * plane + r]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  if (m != -__builtin_inff()) {
+    for (int s = 0; s < p.splits; ++s) {
+      const float w = __builtin_amdgcn_exp2f((p.part_lse[s * plane + r] - m) * LOG2E);
+      sum += w;
+      const f32x4* po = (const f32x4*)(p.part_o + (s * plane + r) * D + 8 * g);
+      const f32x4 a = po[0], bq = po[1];
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += w * a[e];
+        acc[4 + e] += w * bq[e];
+      }
+    }
+  }
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  const size_t bhq = r / p.Nq;
+  const int i = (int)(r - bhq * p.Nq);
+  const int b = (int)(bhq / p.Hq), h = (int)(bhq - (size_t)b * p.Hq);
+  uint8_t* op = p.o + (((size_t)b * p.Nq + i) * p.Hq + h) * (size_t)(D * 2) + 16 * g;
+  u32x4 w;
+  for (int e = 0; e < 4; ++e)
+    w[e] = __builtin_bit_cast(unsigned, T::cvt2(acc[2 * e] * inv, acc[2 * e + 1] * inv));
+  *(u32x4*)op = w;
+  if (g == 0) p.lse[r] = sum > 0.f ? m + __builtin_amdgcn_logf(sum) * LN2 : -__builtin_inff();
 }
 
 }  // namespace fa

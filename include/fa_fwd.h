@@ -57,8 +57,8 @@ enum fa_status {
   FA_ERR_ALIGN = -6,        /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_TOO_LARGE = -7,    /* the work grid or a per-head extent exceeds 2^31 - 1         */
   FA_ERR_LAUNCH = -8,       /* the HIP launch reported an error                            */
-  FA_ERR_WORKSPACE = -9,    /* backward: workspace NULL or smaller than
-                               fa_bwd_workspace_bytes(B, Nq, Hq)                           */
+  FA_ERR_WORKSPACE = -9,    /* workspace NULL, not 16-byte aligned (split-KV) or smaller
+                               than fa_bwd_workspace_bytes / fa_fwd_splitkv_workspace_bytes */
   FA_ERR_PAGE = -10         /* paged K/V: page_size not a positive multiple of 64, or
                                num_pages / max_pages not positive, or a page extent
                                (pages x page_size) above 2^31 - 1                          */
@@ -74,6 +74,39 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
                void* stream);
+
+/* ---- Split-KV forward: more parallel work for short sequences and few heads.
+ *
+ * The pages gain 10-25% at 8 query heads and 1k tokens from a persistent, cluster-aware
+ * tile scheduler ("[RFC] FA4 - head_dim=256 & head_dim=512", feature table of section
+ * "Phase 2": the persistent scheduler gated on short key lengths; "short-sequence perf"
+ * in the same table). On the 256 CUs of an MI355X such shapes leave most CUs idle, so here
+ * the key range of every query tile is cut into num_splits ranges computed by separate
+ * workgroups; each writes its normalised output O_s and log-sum-exp LSE_s (fp32) to the
+ * workspace, and a second kernel merges them exactly:
+ *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) * O_s
+ * The result is the operation of fa_fwd (same layouts, same causal mask, same errors);
+ * only the rounding order of the sums differs.
+ *
+ * workspace: caller-owned device memory of at least
+ *   fa_fwd_splitkv_workspace_bytes(B, Nq, Hq, d, num_splits) = num_splits*B*Hq*Nq*(d+1)*4
+ * bytes, 16-byte aligned; its contents on entry do not matter. num_splits: 1..256 (splits
+ * past the keys of a query tile are empty). fa_fwd_num_splits returns the library's
+ * choice for a shape (1 when the plain grid already fills the GPU). */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits);
+
+int fa_fwd_num_splits(int B, int Nq, int Nk, int Hq, int d, int causal);
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
+                   int num_splits, void* stream);
+
+/* Same as fa_fwd_splitkv with fp16 q/k/v/o. */
+int fa_fwd_splitkv_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* workspace, size_t workspace_bytes,
+                       int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
+                       int num_splits, void* stream);
 
 /* ---- Variable-length batches, per-sequence key counts and a paged K/V cache.
  *

@@ -35,7 +35,8 @@ def test_library_exports_every_header_symbol():
     names = _lib.header_symbols()
     assert set(names) == {"fa_fwd", "fa_fwd_f16", "fa_strerror", "fa_fwd_check", "fa_bwd", "fa_bwd_f16",
                           "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_f16", "fa_fwd_paged",
-                          "fa_fwd_paged_f16"}
+                          "fa_fwd_paged_f16", "fa_fwd_splitkv", "fa_fwd_splitkv_f16",
+                          "fa_fwd_splitkv_workspace_bytes", "fa_fwd_num_splits"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -207,3 +208,51 @@ def test_varlen_python_layer_rejects_cpu_tensors():
         fa.forward_varlen(q, q, q, cu, cu, 10)
     with pytest.raises(ValueError, match="GPU"):
         fa.forward_paged(q, q[None], q[None], cu, cu[1:], cu[None], 10)
+
+
+# ---- split-KV entry points
+
+def _split(fn, **kw):
+    a = dict(GOOD, **kw)
+    splits = a.get("splits", 4)
+    ws = a.get("ws", A + 0x1000)
+    wsb = a.get("wsb", splits * a["B"] * a["Hq"] * a["Nq"] * (a["d"] + 1) * 4)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], ws, wsb, a["B"], a["Nq"], a["Nk"], a["Hq"], a["Hkv"],
+              a["d"], a["causal"], ctypes.c_float(a["scale"]), splits, None)
+
+
+def test_splitkv_workspace_size():
+    lib = _lib.load()
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 300, 8, 128, 3) == 3 * 2 * 8 * 300 * 129 * 4
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 300, 8, 256, 1) == 2 * 8 * 300 * 257 * 4
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 300, 8, 64, 3) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 300, 8, 128, 0) == 0
+
+
+def test_num_splits_choice():
+    # a grid that fills the GPU is not split; few heads and short sequences are
+    assert fa.num_splits(4, 8192, 8192, 8, 256) == 1
+    assert fa.num_splits(32, 1024, 1024, 8, 256) == 1
+    assert fa.num_splits(1, 1024, 1024, 8, 256) > 1
+    assert fa.num_splits(1, 1024, 1024, 8, 256, causal=True) > 1
+    assert fa.num_splits(1, 100, 100, 8, 256) == 1  # too few key tiles to split
+    assert fa.num_splits(4, 1024, 1024, 8, 256) == 1
+    for shape in [(1, 1024, 1024, 8, 256), (1, 1024, 1024, 16, 128), (2, 2048, 2048, 8, 256)]:
+        s = fa.num_splits(*shape)
+        assert 1 <= s <= 4
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd_splitkv", "fa_fwd_splitkv_f16"])
+def test_splitkv_rejects_before_any_hip_call(entry):
+    fn = getattr(_lib.load(), entry)
+    assert _split(fn, q=0) == _lib.FA_ERR_NULL
+    assert _split(fn, d=64) == _lib.FA_ERR_HEADDIM
+    assert _split(fn, causal=1, Nk=17) == _lib.FA_ERR_CAUSAL_SHAPE
+    assert _split(fn, Hkv=3) == _lib.FA_ERR_SHAPE
+    assert _split(fn, splits=0) == _lib.FA_ERR_SHAPE
+    assert _split(fn, splits=257) == _lib.FA_ERR_SHAPE
+    assert _split(fn, scale=math.nan) == _lib.FA_ERR_SCALE
+    assert _split(fn, o=A + 2) == _lib.FA_ERR_ALIGN
+    assert _split(fn, ws=0) == _lib.FA_ERR_WORKSPACE
+    assert _split(fn, ws=A + 4) == _lib.FA_ERR_WORKSPACE
+    assert _split(fn, wsb=4 * 2 * 8 * 300 * 129 * 4 - 1) == _lib.FA_ERR_WORKSPACE

@@ -239,3 +239,21 @@ def test_sample_rows_cover_edges():
         for h in range(3):
             s = set(r[b, h].tolist())
             assert {0, 1, 127, 128, 998, 999} <= s and max(s) < 1000
+
+
+# --- the exact merge of partial results over key ranges (split-KV, and the cross-GPU combine)
+
+def test_partials_over_key_ranges_merge_exactly():
+    # O and LSE over all keys equal the LSE-weighted merge of O_s, LSE_s over disjoint key
+    # ranges: LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s
+    q, k, v = _rand(2, 7, 4, 2, 8, 11, Nk=50)
+    O, L = attention_ref(q, k, v, False, 0.4)
+    cuts = [0, 13, 14, 40, 50]
+    parts = [attention_ref(q, k[:, a:b], v[:, a:b], False, 0.4) for a, b in zip(cuts[:-1], cuts[1:])]
+    Ls = np.stack([p[1] for p in parts])          # [S, B, H, Nq]
+    Os = np.stack([p[0] for p in parts])          # [S, B, Nq, H, d]
+    Lm = np.log(np.exp(Ls).sum(axis=0))
+    w = np.exp(Ls - Lm)                           # [S, B, H, Nq]
+    Om = (w.transpose(0, 1, 3, 2)[..., None] * Os).sum(axis=0)
+    np.testing.assert_allclose(Lm, L, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Om, O, rtol=0, atol=1e-13)

@@ -194,3 +194,47 @@ def test_python_layer_errors_on_gpu_tensors():
         fa.forward(q, k, k, causal=True)
     with pytest.raises(ValueError, match="dtype"):
         fa.forward(q, k.half(), k.half())
+
+
+# ---------------------------------------------------------------- split-KV forward
+
+SPLIT = [
+    # name,           B,  N,    Hq, Hkv, d,  seed, splits
+    ("split2_tail",   1,  777,  4,  2,  128, 91, 2),
+    ("split3_hd256",  1,  700,  2,  1,  256, 92, 3),
+    ("split7",        2,  1024, 2,  2,  128, 93, 7),
+    ("split_many",    1,  300,  2,  1,  256, 94, 64),   # more splits than key tiles: empty ranges
+    ("pages_8heads",  1,  1024, 8,  8,  256, 95, None), # the library's choice at 8 heads, 1k tokens
+]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("case", SPLIT, ids=[c[0] for c in SPLIT])
+def test_splitkv_full_rows(case, causal):
+    name, B, N, Hq, Hkv, d, seed, splits = case
+    q, k, v = W.make_qkv(B, N, N, Hq, Hkv, d, seed)
+    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    ns = fa.num_splits(B, N, N, Hq, d, causal) if splits is None else splits
+    _say(f"[gpu] splitkv {name} B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} causal={causal} splits={ns}")
+    o, lse = fa.forward_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, num_splits=ns)
+    torch.cuda.synchronize()
+    O_ref, L_ref = attention_ref(q, k, v, causal, scale)
+    _compare(name, o, lse, O_ref, L_ref)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_splitkv_one_split_equals_plain_bitwise(d):
+    q, k, v = W.make_qkv(2, 515, 515, 4, 2, d, 96)
+    for causal in (False, True):
+        o1, l1 = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+        o2, l2 = fa.forward_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=causal, num_splits=1)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), (d, causal)
+
+
+def test_splitkv_fp16():
+    q, k, v = W.make_qkv(1, 900, 900, 2, 1, 256, 97, dtype=torch.float16)
+    o, lse = fa.forward_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=True, num_splits=5)
+    torch.cuda.synchronize()
+    O_ref, L_ref = attention_ref(q, k, v, True, 1.0 / 16)
+    _compare("splitkv_fp16", o, lse, O_ref, L_ref)
