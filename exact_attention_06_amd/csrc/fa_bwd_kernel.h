@@ -49,6 +49,7 @@ struct BwdParams {
 template <int D>
 struct BwdCfg {
   static constexpr int NW = 4;         // waves per workgroup, 32 rows each
+  static constexpr int WPE = D == 128 ? 2 : 1;  // waves per SIMD the registers are sized for
   static constexpr int BT = 32;        // rows per streamed tile
   static constexpr int ROW = D * 2 + 16;  // padded LDS row pitch (bytes)
   static constexpr int TB = BT * ROW;     // bytes per streamed tile
@@ -93,7 +94,11 @@ bwd_dq_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int bh = blockIdx.x / p.ntile, qt = blockIdx.x % p.ntile;
+  // causal: the last query tiles see the most keys; they start first (longest-first), with
+  // consecutive blocks on consecutive heads
+  const int nbh = p.B * p.Hq;
+  const int bh = CAUSAL ? (int)(blockIdx.x % nbh) : (int)(blockIdx.x / p.ntile);
+  const int qt = CAUSAL ? p.ntile - 1 - (int)(blockIdx.x / nbh) : (int)(blockIdx.x % p.ntile);
   const int b = bh / p.Hq, hq = bh % p.Hq, kvh = hq / p.group;
   const int Nq = p.Nq, Nk = p.Nk;
   const int q_wg0 = qt * BR, qw0 = q_wg0 + wave * 32, q_lane = qw0 + l32;
@@ -218,7 +223,7 @@ bwd_dq_kernel(BwdParams p) {
 // dkdv kernel: one workgroup per (b, kvh, 128-key tile); Q/dO tiles of BT queries stream
 // through LDS for every query head of the group.
 template <int D, bool CAUSAL, class T>
-__global__ void __launch_bounds__(BwdCfg<D>::NW * 64)
+__global__ void __launch_bounds__(BwdCfg<D>::NW * 64, BwdCfg<D>::WPE)
 bwd_dkdv_kernel(BwdParams p) {
   using x8 = typename T::x8;
   using x2 = typename T::x2;
@@ -232,7 +237,10 @@ bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int bk = blockIdx.x / p.ntile, kt = blockIdx.x % p.ntile;
+  // causal: the first key tiles are seen by the most queries; they start first
+  const int nbk = p.B * p.Hkv;
+  const int bk = CAUSAL ? (int)(blockIdx.x % nbk) : (int)(blockIdx.x / p.ntile);
+  const int kt = CAUSAL ? (int)(blockIdx.x / nbk) : (int)(blockIdx.x % p.ntile);
   const int b = bk / p.Hkv, kvh = bk % p.Hkv;
   const int Nq = p.Nq, Nk = p.Nk;
   const int k_wg0 = kt * BK, kw0 = k_wg0 + wave * 32, k_lane = kw0 + l32;
