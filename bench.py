@@ -23,6 +23,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA peak (published)
 DEFAULT_WORKLOAD = "hd256_N8192"
 PAGES_B200 = {  # pages' own forward TFLOPS for the hd256 snapshot workloads (B200, context only)
@@ -287,6 +288,38 @@ def main():
                 log(f"[short] B={B_} N={N_} Hq={H_} d={d_} {'causal' if c else 'noncausal':9s} plain "
                     f"{ent['plain_tflops']:7.1f} TFLOPS, split-KV x{ns} {ent['splitkv_tflops']:7.1f} TFLOPS")
 
+    # fp8 (e4m3) inputs, one dequantisation factor per tensor, bf16 output; priced against the
+    # fp8 MFMA peak
+    fp8 = []
+    if not args.no_sweep:
+        for name in ("hd128_N8192_mha", "hd256_N8192"):
+            x = W.by_name(name)
+            qx, kx, vx = gpu_inputs(x, torch)
+            sc = [float(t.abs().max()) / 224.0 for t in (qx, kx, vx)]
+            q8, k8, v8 = ((t.float() / s_).to(torch.float8_e4m3fn) for t, s_ in zip((qx, kx, vx), sc))
+            del qx, kx, vx
+            for c in (False, True):
+                call = lambda: fa.forward_fp8(q8, k8, v8, sc[0], sc[1], sc[2], causal=c, scale=x.scale)
+                for _ in range(2):
+                    call()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                n = max(1, args.sweep_steps)
+                e0.record()
+                for _ in range(n):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
+                m = e0.elapsed_time(e1) / n
+                t = x.flops(c) / (m * 1e-3) / 1e12
+                fp8.append({"workload": x.name, "causal": c, "ms": round(m, 4), "tflops": round(t, 1),
+                            "frac_fp8_peak": round(t / PEAK_FP8_TFLOPS, 4)})
+                log(f"[fp8] {x.name:20s} {'causal' if c else 'noncausal':9s} {m:8.3f} ms {t:7.1f} TFLOPS "
+                    f"{100 * t / PEAK_FP8_TFLOPS:5.1f}% of {PEAK_FP8_TFLOPS:.0f}")
+            del q8, k8, v8
+            torch.cuda.empty_cache()
+
     # serving variants: packed variable-length prefill, paged prefill, paged decode
     variants = []
     if not args.no_sweep:
@@ -354,6 +387,7 @@ def main():
         "backward": backward,
         "variants": variants,
         "short_splitkv": short,
+        "fp8": fp8,
         "kernel_source_hash": kernel_source_hash(),
     }
     if b200:

@@ -23,8 +23,8 @@ import math
 
 from . import _lib
 
-__all__ = ["forward", "forward_splitkv", "num_splits", "backward", "forward_varlen", "forward_paged",
-           "check_args", "FaError"]
+__all__ = ["forward", "forward_fp8", "forward_splitkv", "num_splits", "backward", "forward_varlen",
+           "forward_paged", "check_args", "FaError"]
 
 
 class FaError(ValueError):
@@ -87,6 +87,40 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), float(scale), stream)
+    if rc != 0:
+        _raise(rc)
+    return out, lse
+
+
+def forward_fp8(q, k, v, q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0,
+                causal: bool = False, scale: float | None = None):
+    """Forward pass on e4m3 inputs (fa_fwd_fp8): q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] as
+    torch.float8_e4m3fn with one dequantisation factor each; returns o [B, Nq, Hq, d] in
+    bfloat16 and lse [B, Hq, Nq] (fp32) of attention on q_scale*q, k_scale*k, v_scale*v."""
+    import torch
+
+    lib = _lib.load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [batch, seq, heads, head_dim]")
+        if t.dtype != torch.float8_e4m3fn:
+            raise ValueError(f"{name} must be torch.float8_e4m3fn")
+        if t.device != q.device:
+            raise ValueError("q, k and v must be on one device")
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q/k/v shapes do not match: q [B,Nq,Hq,d], k and v [B,Nk,Hkv,d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((B, Nq, Hq, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            float(q_scale), float(k_scale), float(v_scale), B, Nq, Nk, Hq, Hkv, d,
+                            int(bool(causal)), float(scale), stream)
     if rc != 0:
         _raise(rc)
     return out, lse

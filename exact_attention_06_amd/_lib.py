@@ -60,6 +60,9 @@ def load():
                 fn = getattr(lib, name)
                 fn.argtypes = args
                 fn.restype = _I
+        lib.fa_fwd_fp8.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                   _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+        lib.fa_fwd_fp8.restype = _I
         for name in ("fa_fwd_splitkv", "fa_fwd_splitkv_f16"):
             fn = getattr(lib, name)
             fn.argtypes = _SPLIT_ARGS

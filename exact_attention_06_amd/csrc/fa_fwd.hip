@@ -12,6 +12,7 @@
 #include "fa_fwd.h"
 #include "fa_kernel.h"
 #include "fa_bwd_kernel.h"
+#include "fa_fp8_kernel.h"
 
 namespace {
 
@@ -51,6 +52,53 @@ void clear_extras(fa::FwdParams& prm) {
   prm.total_q = prm.total_k = prm.page_size = prm.max_pages = prm.num_pages = 0;
   prm.part_o = prm.part_lse = nullptr;
   prm.splits = prm.tps = 0;
+  prm.v_scale = 1.f;
+}
+
+// ---- fp8 (e4m3) forward
+template <int D, bool CAUSAL>
+int launch_fp8(const fa::FwdParams& prm, hipStream_t stream) {
+  const int grid = prm.B * prm.Hq * prm.nqt;
+  hipLaunchKernelGGL((fa::fwd_fp8_kernel<D, CAUSAL>), dim3(grid), dim3(fa::Fp8Cfg<D>::NW * 64), 0, stream, prm);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, float q_scale, float k_scale,
+            float v_scale, int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (d != 128 && d != 256) return FA_ERR_HEADDIM;
+  if (causal && Nq != Nk) return FA_ERR_CAUSAL_SHAPE;
+  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  for (float x : {q_scale, k_scale, v_scale})
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_SCALE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
+  if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
+  const int64_t BR = fa::Fp8Cfg<128>::BR;
+  if ((int64_t)B * Hq * ((Nq + BR - 1) / BR) > INT_MAX || (int64_t)Nq + BR > INT_MAX ||
+      (int64_t)Nk + 256 > INT_MAX)
+    return FA_ERR_TOO_LARGE;
+  fa::FwdParams prm;
+  prm.q = (const uint8_t*)q;
+  prm.k = (const uint8_t*)k;
+  prm.v = (const uint8_t*)v;
+  prm.o = (uint8_t*)o;
+  prm.lse = lse;
+  prm.B = B;
+  prm.Nq = Nq;
+  prm.Nk = Nk;
+  prm.Hq = Hq;
+  prm.Hkv = Hkv;
+  prm.group = Hq / Hkv;
+  clear_extras(prm);
+  const float c = scale * q_scale * k_scale * fa::LOG2E;
+  prm.zero_scores = !(c >= FLT_MIN);
+  prm.c = prm.zero_scores ? fa::LOG2E : c;
+  prm.v_scale = v_scale;
+  prm.nqt = (Nq + (int)BR - 1) / (int)BR;
+  hipStream_t s = (hipStream_t)stream;
+  if (d == 128) return causal ? launch_fp8<128, true>(prm, s) : launch_fp8<128, false>(prm, s);
+  return causal ? launch_fp8<256, true>(prm, s) : launch_fp8<256, false>(prm, s);
 }
 
 template <int D> int br() { return fa::Layout<D>::BR; }
@@ -323,6 +371,12 @@ int fa_fwd_paged_f16(const void* q, const void* k_cache, const void* v_cache, vo
                           stream, true);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, float q_scale, float k_scale,
+               float v_scale, int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
+               void* stream) {
+  return run_fp8(q, k, v, o, lse, q_scale, k_scale, v_scale, B, Nq, Nk, Hq, Hkv, d, causal, scale, stream);
+}
+
 size_t fa_fwd_splitkv_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits) {
   return splitkv_ws_bytes(B, Nq, Hq, d, num_splits);
 }
@@ -368,7 +422,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_SHAPE: return "B, Nq, Nk, Hq and Hkv must be positive and Hq a multiple of Hkv";
     case FA_ERR_HEADDIM: return "head dim must be 128 or 256";
     case FA_ERR_CAUSAL_SHAPE: return "causal attention needs Nq == Nk";
-    case FA_ERR_SCALE: return "scale must be finite and non-negative";
+    case FA_ERR_SCALE: return "scale must be finite and non-negative (fp8 dequantisation factors finite and positive)";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_TOO_LARGE: return "problem too large for 32-bit grid or sequence indexing";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";

@@ -122,6 +122,8 @@ struct FwdParams {
   float* part_o;
   float* part_lse;
   int splits, tps;
+  // fp8 inputs (fwd_fp8_kernel): O is multiplied by v_scale; q and k scales are folded into c
+  float v_scale;
 };
 
 template <bool V> struct BoolC { static constexpr bool value = V; };

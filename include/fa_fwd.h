@@ -75,6 +75,22 @@ int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
                void* stream);
 
+/* ---- FP8 inputs: q, k, v in e4m3 (OCP FP8, 1 byte per element), o in bf16.
+ *
+ * The FP8 input path of the pages ("[RFC] FA4 - head_dim=256 & head_dim=512", feature
+ * table of section "Phase 2": FP8 input on the FP8 tensor-core MMA). Layouts, shapes,
+ * causal mask and LSE are those of fa_fwd; the operation is fa_fwd's on the dequantised
+ * inputs q_scale*Q, k_scale*K, v_scale*V (one positive factor per tensor). Q K^T is exact
+ * (fp8 products accumulate in fp32); the softmax weights P are rounded to e4m3 for P V
+ * (3 mantissa bits: up to 2^-4 relative, 2^-10 absolute below 2^-6) and O is normalised
+ * by the fp32 sum of those rounded weights; the LSE uses the fp32 sum of the unrounded
+ * ones. Errors: as fa_fwd; FA_ERR_SCALE also for a dequantisation factor that is not
+ * finite and positive. */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               float q_scale, float k_scale, float v_scale,
+               int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
+               void* stream);
+
 /* ---- Split-KV forward: more parallel work for short sequences and few heads.
  *
  * The pages gain 10-25% at 8 query heads and 1k tokens from a persistent, cluster-aware

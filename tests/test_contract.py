@@ -36,7 +36,7 @@ def test_library_exports_every_header_symbol():
     assert set(names) == {"fa_fwd", "fa_fwd_f16", "fa_strerror", "fa_fwd_check", "fa_bwd", "fa_bwd_f16",
                           "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_f16", "fa_fwd_paged",
                           "fa_fwd_paged_f16", "fa_fwd_splitkv", "fa_fwd_splitkv_f16",
-                          "fa_fwd_splitkv_workspace_bytes", "fa_fwd_num_splits"}
+                          "fa_fwd_splitkv_workspace_bytes", "fa_fwd_num_splits", "fa_fwd_fp8"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -256,3 +256,31 @@ def test_splitkv_rejects_before_any_hip_call(entry):
     assert _split(fn, ws=0) == _lib.FA_ERR_WORKSPACE
     assert _split(fn, ws=A + 4) == _lib.FA_ERR_WORKSPACE
     assert _split(fn, wsb=4 * 2 * 8 * 300 * 129 * 4 - 1) == _lib.FA_ERR_WORKSPACE
+
+
+def _fp8(**kw):
+    a = dict(GOOD, **kw)
+    return _lib.load().fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a.get("qs", 0.5),
+                                  a.get("ks", 0.25), a.get("vs", 2.0), a["B"], a["Nq"], a["Nk"], a["Hq"],
+                                  a["Hkv"], a["d"], a["causal"], ctypes.c_float(a["scale"]), None)
+
+
+def test_fp8_rejects_before_any_hip_call():
+    assert _fp8(k=0) == _lib.FA_ERR_NULL
+    assert _fp8(d=64) == _lib.FA_ERR_HEADDIM
+    assert _fp8(causal=1, Nk=17) == _lib.FA_ERR_CAUSAL_SHAPE
+    assert _fp8(Hkv=3) == _lib.FA_ERR_SHAPE
+    assert _fp8(scale=math.nan) == _lib.FA_ERR_SCALE
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        assert _fp8(qs=bad) == _lib.FA_ERR_SCALE
+        assert _fp8(ks=bad) == _lib.FA_ERR_SCALE
+        assert _fp8(vs=bad) == _lib.FA_ERR_SCALE
+    assert _fp8(v=A + 8) == _lib.FA_ERR_ALIGN
+    assert _fp8(lse=A + 2) == _lib.FA_ERR_ALIGN
+    assert _fp8(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 12, Nk=1 << 12) == _lib.FA_ERR_TOO_LARGE
+
+
+def test_fp8_python_layer_checks_dtype():
+    q = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward_fp8(q, q, q)
