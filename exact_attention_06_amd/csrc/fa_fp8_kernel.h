@@ -214,7 +214,7 @@ fwd_fp8_kernel(FwdParams p) {
   // 8w + e is score register 8(w%2) + e of score tile w/2
   auto softmax = [&](const f32x16 (&s)[MT1], i32x8& pb) {
     const float negm = -m_run;
-    float sum0 = 0.f, sum1 = 0.f;
+    float sum0, sum1;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
@@ -223,8 +223,13 @@ fwd_fp8_kernel(FwdParams p) {
         float pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r + e], c, negm));
-        sum0 += pv[0] + pv[2];
-        sum1 += pv[1] + pv[3];
+        if (w == 0 && h == 0) {
+          sum0 = pv[0] + pv[2];
+          sum1 = pv[1] + pv[3];
+        } else {
+          sum0 += pv[0] + pv[2];
+          sum1 += pv[1] + pv[3];
+        }
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
         pb[2 * w + h] = word;

@@ -13,6 +13,7 @@
 #include "fa_kernel.h"
 #include "fa_bwd_kernel.h"
 #include "fa_fp8_kernel.h"
+#include "fa_hd512_kernel.h"
 
 namespace {
 
@@ -103,26 +104,35 @@ int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, fl
 
 template <int D> int br() { return fa::Layout<D>::BR; }
 
+// hd512: head dim 512 is accepted (the dense forward pass only)
 int check(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
-          int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale) {
+          int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale, bool hd512 = false) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
-  if (d != 128 && d != 256) return FA_ERR_HEADDIM;
+  if (d != 128 && d != 256 && !(hd512 && d == 512)) return FA_ERR_HEADDIM;
   if (causal && Nq != Nk) return FA_ERR_CAUSAL_SHAPE;
   if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
   if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
-  const int64_t BR = d == 128 ? br<128>() : br<256>();
+  const int64_t BR = d == 128 ? br<128>() : d == 256 ? br<256>() : fa::Hd512::BR;
   const int64_t nqt = (Nq + BR - 1) / BR;
   const int64_t grid = (int64_t)B * Hq * nqt;
   if (grid > INT_MAX || (int64_t)Nq + BR > INT_MAX || (int64_t)Nk + 256 > INT_MAX) return FA_ERR_TOO_LARGE;
   return FA_OK;
 }
 
+template <bool CAUSAL, class T>
+int launch_hd512(fa::FwdParams& prm, hipStream_t stream) {
+  prm.nqt = (prm.Nq + fa::Hd512::BR - 1) / fa::Hd512::BR;
+  hipLaunchKernelGGL((fa::fwd_hd512_kernel<CAUSAL, T>), dim3(prm.B * prm.Hq * prm.nqt), dim3(fa::Hd512::NW * 64), 0,
+                     stream, prm);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 template <class T>
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq, int Nk,
         int Hq, int Hkv, int d, int causal, float scale, void* stream) {
-  const int st = check(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale);
+  const int st = check(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale, true);
   if (st != FA_OK) return st;
   fa::FwdParams prm;
   prm.q = (const uint8_t*)q;
@@ -138,6 +148,8 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   prm.group = Hq / Hkv;
   clear_extras(prm);
   set_scale(prm, scale);
+  if (d == 512)
+    return causal ? launch_hd512<true, T>(prm, (hipStream_t)stream) : launch_hd512<false, T>(prm, (hipStream_t)stream);
   return dispatch<0, T>(prm, d, causal, (hipStream_t)stream);
 }
 
@@ -326,7 +338,7 @@ extern "C" {
 
 int fa_fwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
                  int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale) {
-  return check(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale);
+  return check(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale, true);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq, int Nk,
@@ -420,7 +432,7 @@ const char* fa_strerror(int code) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a pointer argument is NULL";
     case FA_ERR_SHAPE: return "B, Nq, Nk, Hq and Hkv must be positive and Hq a multiple of Hkv";
-    case FA_ERR_HEADDIM: return "head dim must be 128 or 256";
+    case FA_ERR_HEADDIM: return "head dim must be 128 or 256 (or 512 for fa_fwd / fa_fwd_f16)";
     case FA_ERR_CAUSAL_SHAPE: return "causal attention needs Nq == Nk";
     case FA_ERR_SCALE: return "scale must be finite and non-negative (fp8 dequantisation factors finite and positive)";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";

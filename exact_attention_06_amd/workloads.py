@@ -10,7 +10,8 @@ Workload shapes follow the pages:
   * "h3-blackwell-runtime/FLASH4.md", "GB10 Validation" table: [1, 257, 8, 128]
     and [1, 20480, 56, 128] in [batch, seq, heads, head_dim];
   * "[RFC] FA4 - head_dim=256 & head_dim=512", "Performance Snapshot": head_dim 256,
-    8 query heads, batch sized to about 32k tokens, sequence lengths 1k..128k.
+    8 query heads, batch sized to about 32k tokens, sequence lengths 1k..128k; the same
+    shape at head_dim 512, which the page's "Phase 4" table lists without shapes.
 The head_dim=128 sweep (16 query heads, MHA and 4:1 GQA) and the spiked-key video
 shape (every 16th key scaled by 4, to make peaked softmax rows) are synthetic
 stand-ins with the same structure; there is no dataset behind any of them.
@@ -23,7 +24,7 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = ["Workload", "make_qkv", "sample_rows", "tiny", "ragged", "hd128_sweep",
-           "hd256_sweep", "video", "all_workloads", "by_name", "VarWorkload", "make_varlen",
+           "hd256_sweep", "hd512_sweep", "video", "all_workloads", "by_name", "VarWorkload", "make_varlen",
            "make_paged", "var_workloads", "var_inputs"]
 
 TOKENS = 32768  # batch is sized so that B * N is about this many tokens
@@ -110,13 +111,23 @@ def hd256_sweep():
     return out
 
 
+def hd512_sweep():
+    """Head dim 512 (the pages list it as a planned extended head dim, with no shapes of its
+    own): the hd256 snapshot's shape - 8 query heads, about 32k tokens - at d = 512."""
+    out = []
+    for i, N in enumerate([1024, 2048, 4096, 8192, 16384, 32768]):
+        out.append(Workload(f"hd512_N{N}", B=max(1, TOKENS // N), N=N, Hq=8, Hkv=8, d=512,
+                            seed=60 + i, full_oracle=False))
+    return out
+
+
 def video():
     return Workload("video", B=1, N=20480, Hq=56, Hkv=56, d=128, seed=5, causal_modes=(False,),
                     k_spike=True, full_oracle=False)
 
 
 def all_workloads():
-    return [tiny(), ragged()] + hd128_sweep() + hd256_sweep() + [video()]
+    return [tiny(), ragged()] + hd128_sweep() + hd256_sweep() + [video()] + hd512_sweep()
 
 
 def by_name(name):

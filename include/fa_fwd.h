@@ -18,7 +18,8 @@
  *     and an error (never a silent kernel change) on any contract violation:
  *     "h3-blackwell-runtime/FLASH4.md", section "API";
  *   - head_dim 256 next to 128, causal and non-causal variants: "[RFC] FA4 - head_dim=256 &
- *     head_dim=512", sections "Overview" and "Performance Snapshot";
+ *     head_dim=512", sections "Overview" and "Performance Snapshot"; head_dim 512 (fa_fwd
+ *     and fa_fwd_f16 only): the same page, table of section "Phase 4";
  *   - grouped-query heads sharing one K/V head: the Dutch page's compatibility section.
  *   The pages never define the LSE output; it is the natural-log log-sum-exp of the scaled
  *   scores over the visible keys, in fp32.
@@ -50,7 +51,7 @@ enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,         /* a pointer argument is NULL                                  */
   FA_ERR_SHAPE = -2,        /* B, Nq, Nk, Hq or Hkv <= 0, or Hq % Hkv != 0                 */
-  FA_ERR_HEADDIM = -3,      /* d is not 128 or 256                                         */
+  FA_ERR_HEADDIM = -3,      /* d is not 128 or 256 (fa_fwd and fa_fwd_f16: or 512)         */
   FA_ERR_CAUSAL_SHAPE = -4, /* causal with Nq != Nk (the causal alignment is defined for
                                square problems only)                                       */
   FA_ERR_SCALE = -5,        /* scale is NaN, infinite or negative                          */
@@ -65,7 +66,8 @@ enum fa_status {
 };
 
 /* Forward pass, bf16 q/k/v/o, fp32 LSE. Arguments as described above; `scale` multiplies
- * the q.k dot products (1/sqrt(d) is the usual choice). Returns an fa_status. */
+ * the q.k dot products (1/sqrt(d) is the usual choice). d is 128, 256 or 512. Returns an
+ * fa_status. */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
            void* stream);

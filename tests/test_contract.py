@@ -60,9 +60,23 @@ def test_bad_shape(kw):
     assert _check(**kw) == _lib.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("d", [0, 64, 96, 127, 192, 512])
+@pytest.mark.parametrize("d", [0, 64, 96, 127, 192, 384, 1024])
 def test_bad_head_dim(d):
     assert _check(d=d) == _lib.FA_ERR_HEADDIM
+
+
+def test_head_dim_512_only_for_the_dense_forward():
+    # d = 512 runs on the dense forward kernel only; every other entry point rejects it
+    assert _check(d=512) == _lib.FA_OK
+    assert _check(d=512, causal=1, Hkv=8) == _lib.FA_OK
+    lib = _lib.load()
+    assert _bwd(lib.fa_bwd, d=512) == _lib.FA_ERR_HEADDIM
+    assert _varlen(lib.fa_fwd_varlen, d=512) == _lib.FA_ERR_HEADDIM
+    assert _paged(lib.fa_fwd_paged, d=512) == _lib.FA_ERR_HEADDIM
+    assert _split(lib.fa_fwd_splitkv, d=512) == _lib.FA_ERR_HEADDIM
+    assert _fp8(d=512) == _lib.FA_ERR_HEADDIM
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 300, 8, 512, 2) == 0
+    assert lib.fa_fwd_num_splits(1, 1024, 1024, 8, 512, 0) == 1
 
 
 def test_causal_needs_square():

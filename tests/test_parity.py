@@ -83,6 +83,10 @@ SMALL = [
     ("one_token",      1,    1,    1,  1,  1, 128, 24),
     ("few_tokens",     2,    3,    3,  4,  1, 256, 25),
     ("mqa_hd128",      1,  300,  300,  8,  1, 128, 26),
+    ("hd512_tiny",     1,  256,  256,  2,  2, 512, 27),
+    ("hd512_tail300",  1,  300,  300,  4,  2, 512, 28),
+    ("hd512_few",      2,    3,    3,  4,  1, 512, 29),
+    ("hd512_tail1000", 1, 1000, 1000,  2,  1, 512, 30),
 ]
 
 
@@ -98,6 +102,8 @@ RECT = [
     ("q_long_k_short", 1, 1100, 70, 4, 4, 128, 32),
     ("hd256_rect", 2, 33, 517, 2, 2, 256, 33),
     ("k_single", 1, 65, 1, 2, 1, 256, 34),
+    ("hd512_rect", 1, 200, 333, 2, 2, 512, 35),
+    ("hd512_k_single", 1, 130, 1, 2, 1, 512, 36),
 ]
 
 
@@ -108,7 +114,7 @@ def test_rectangular_noncausal(case):
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [128, 256, 512])
 def test_fp16_entry_point(d, causal):
     _run_full(f"fp16_d{d}", 1, 513, 513, 4, 2, d, causal, 41 + d, dtype=torch.float16)
 
@@ -133,7 +139,7 @@ def test_workload_sampled_rows(w):
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [128, 256, 512])
 def test_zero_scale(d, causal):
     # scale 0: every visible key gets the same weight (O = mean of the visible V rows,
     # LSE = ln(number of visible keys)); 257 keys leave a masked tail in the last tile
@@ -148,7 +154,7 @@ def test_named_small_workloads(w):
 
 # ---------------------------------------------------------------- exact GPU-side properties
 
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [128, 256, 512])
 def test_gqa_equals_repeated_mha_bitwise(d):
     q, k, v = W.make_qkv(2, 700, 700, 8, 2, d, seed=51)
     _say(f"[gpu] gqa-vs-mha d={d}")
@@ -161,7 +167,7 @@ def test_gqa_equals_repeated_mha_bitwise(d):
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [128, 256, 512])
 def test_value_scaling_is_exact(d):
     q, k, v = W.make_qkv(1, 600, 600, 4, 4, d, seed=52)
     _say(f"[gpu] v-scaling d={d}")
