@@ -204,7 +204,7 @@ def main():
 
     sweep = []
     if not args.no_sweep:
-        pts = [x for x in W.hd128_sweep() + W.hd256_sweep()]
+        pts = [x for x in W.hd128_sweep() + W.hd256_sweep() + W.hd512_sweep()]
         for x in pts:
             qx, kx, vx = gpu_inputs(x, torch)
             for c in (False, True):
