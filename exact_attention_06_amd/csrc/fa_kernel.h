@@ -423,8 +423,31 @@ fwd_kernel(FwdParams p) {
   // GEMM1 walks the head dim with its score tiles innermost, GEMM2 the keys with its output
   // tiles innermost (a dependent MFMA chain issues at nearly full rate on gfx950, so a single
   // score tile needs no split accumulator).
+  // SEQ: LDS fragments are read SPF MFMAs ahead in a fixed order (sched_barrier), so that the
+  // read latency hides under the MFMAs before them; left to itself the compiler read them one
+  // or two MFMAs ahead.
+  constexpr int SPF1 = 4, SPF2 = 4;
   auto gemm1 = [&](int buf, f32x16 (&s)[MT1]) {
     const uint8_t* kl = (buf ? k_lds1 : k_lds0) + k_rd;
+    if constexpr (TileCfg<D>::MODE == SEQ) {
+      constexpr int N = KS1 * MT1;
+      auto frag = [&](const int i) -> x8 {
+        const int t = i / MT1, mt = i % MT1;
+        return __builtin_bit_cast(x8, *(const u32x4*)(kl + mt * 32 * KROW + t * 32));
+      };
+      x8 kf[N];
+#pragma unroll
+      for (int i = 0; i < SPF1; ++i) kf[i] = frag(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if (i + SPF1 < N) kf[i + SPF1] = frag(i + SPF1);
+        const int t = i / MT1, mt = i % MT1;
+        s[mt] = T::mfma(kf[i], qf[t], t == 0 ? f32x16{} : s[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
 #pragma unroll
     for (int mt = 0; mt < MT1; ++mt) s[mt] = f32x16{};
 #pragma unroll
@@ -436,8 +459,38 @@ fwd_kernel(FwdParams p) {
       }
   };
 
+  // V^T fragment i of GEMM2 (k-step i / MT2, output tile i % MT2) from V buffer `buf`
+  auto vfrag = [&](int buf, const int i) -> x8 {
+    const uint8_t* vl = (buf ? v_lds1 : v_lds0) + v_rd;
+    const int u = i / MT2, md = i % MT2;
+    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * u) * VROW + md * 64));
+    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * u + 8) * VROW + md * 64));
+    u32x4 raw;
+    raw[0] = __builtin_bit_cast(u32x2, lo4)[0];
+    raw[1] = __builtin_bit_cast(u32x2, lo4)[1];
+    raw[2] = __builtin_bit_cast(u32x2, hi4)[0];
+    raw[3] = __builtin_bit_cast(u32x2, hi4)[1];
+    return __builtin_bit_cast(x8, raw);
+  };
   auto gemm2 = [&](int buf, const x8 (&pf)[KS2], const x8* pl) {
     const uint8_t* vl = (buf ? v_lds1 : v_lds0) + v_rd;
+    if constexpr (TileCfg<D>::MODE == SEQ) {
+      constexpr int N = KS2 * MT2;
+      auto frag = [&](const int i) -> x8 { return vfrag(buf, i); };
+      x8 vf[N];
+#pragma unroll
+      for (int i = 0; i < SPF2; ++i) vf[i] = frag(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if (i + SPF2 < N) vf[i + SPF2] = frag(i + SPF2);
+        const int u = i / MT2, md = i % MT2;
+        acc[md] = T::mfma(vf[i], pf[u], acc[md]);
+        if (pl) acc[md] = T::mfma(vf[i], pl[u], acc[md]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < KS2; ++u)
 #pragma unroll
