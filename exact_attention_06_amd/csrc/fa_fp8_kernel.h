@@ -146,29 +146,47 @@ fwd_fp8_kernel(FwdParams p) {
   const int v_rd = vrow * ROW + 16 * (g16 ^ (fv & 1)) + 8 * p2;  // + 32 (md ^ (fv >> 1))
   const int v_x = 32 * (fv >> 1);
 
+  // hd128: LDS fragments are read PF MFMAs ahead in a fixed order (sched_barrier), so that the
+  // read latency hides under the MFMAs before them (+7%). hd256 has no registers to spare for
+  // that (the fragments spill and it runs up to 40% slower): there the compiler orders the reads.
+  constexpr int PF = D == 128 ? 2 : 0;
   auto gemm1 = [&](const uint8_t* kl, f32x16 (&s)[MT1]) {
-#pragma unroll
-    for (int mt = 0; mt < MT1; ++mt) s[mt] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < KS1; ++t) {
+    constexpr int N = KS1 * MT1;
+    auto frag = [&](const int i) -> i32x8 {
+      const int t = i / MT1, mt = i % MT1;
       const int o0 = 16 * ((4 * t + 2 * hh) ^ fk), o1 = 16 * ((4 * t + 2 * hh + 1) ^ fk);
-#pragma unroll
-      for (int mt = 0; mt < MT1; ++mt) {
-        const uint8_t* rp = kl + k_rd + mt * 32 * ROW;
-        const u32x4 lo = *(const u32x4*)(rp + o0);
-        const u32x4 hi = *(const u32x4*)(rp + o1);
-        i32x8 a;
-        for (int e = 0; e < 4; ++e) {
-          a[e] = (int)lo[e];
-          a[4 + e] = (int)hi[e];
-        }
-        s[mt] = mfma_fp8(a, qf[t], s[mt]);
+      const uint8_t* rp = kl + k_rd + mt * 32 * ROW;
+      const u32x4 lo = *(const u32x4*)(rp + o0);
+      const u32x4 hi = *(const u32x4*)(rp + o1);
+      i32x8 a;
+      for (int e = 0; e < 4; ++e) {
+        a[e] = (int)lo[e];
+        a[4 + e] = (int)hi[e];
       }
+      return a;
+    };
+    if constexpr (PF == 0) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int t = i / MT1, mt = i % MT1;
+        s[mt] = mfma_fp8(frag(i), qf[t], t == 0 ? f32x16{} : s[mt]);
+      }
+      return;
+    }
+    i32x8 kf[N];
+#pragma unroll
+    for (int i = 0; i < PF && i < N; ++i) kf[i] = frag(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + PF < N) kf[i + PF] = frag(i + PF);
+      const int t = i / MT1, mt = i % MT1;
+      s[mt] = mfma_fp8(kf[i], qf[t], t == 0 ? f32x16{} : s[mt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto gemm2 = [&](const uint8_t* vl, const i32x8& pb) {
-#pragma unroll
-    for (int md = 0; md < MT2; ++md) {
+    auto frag = [&](const int md) -> i32x8 {
       const uint8_t* base = vl + v_rd + ((32 * md) ^ v_x);
       i32x8 a;
 #pragma unroll
@@ -178,7 +196,23 @@ fwd_fp8_kernel(FwdParams p) {
         a[2 * w] = r[0];
         a[2 * w + 1] = r[1];
       }
-      acc[md] = mfma_fp8(a, pb, acc[md]);
+      return a;
+    };
+    if constexpr (PF == 0) {
+#pragma unroll
+      for (int md = 0; md < MT2; ++md) acc[md] = mfma_fp8(frag(md), pb, acc[md]);
+      acc[MT2] = mfma_fp8(ones, pb, acc[MT2]);
+      return;
+    }
+    i32x8 vf[MT2];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) vf[i] = frag(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int md = 0; md < MT2; ++md) {
+      if (md + PF < MT2) vf[md + PF] = frag(md + PF);
+      acc[md] = mfma_fp8(vf[md], pb, acc[md]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     acc[MT2] = mfma_fp8(ones, pb, acc[MT2]);
   };
