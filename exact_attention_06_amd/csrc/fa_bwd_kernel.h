@@ -55,6 +55,28 @@ struct BwdCfg {
   static constexpr int TB = BT * ROW;     // bytes per streamed tile
 };
 
+// A transposed MFMA operand (8 values of one column over 16 rows) from an LDS tile with row
+// pitch `row`: two ds_read_b64_tr_b16, rows 0..7 and 8..15 below `p`.
+template <class X8>
+__device__ __forceinline__ X8 bwd_tr_frag(const uint8_t* p, int row) {
+  const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * row));
+  u32x4 raw;
+  raw[0] = __builtin_bit_cast(u32x2, lo4)[0];
+  raw[1] = __builtin_bit_cast(u32x2, lo4)[1];
+  raw[2] = __builtin_bit_cast(u32x2, hi4)[0];
+  raw[3] = __builtin_bit_cast(u32x2, hi4)[1];
+  return __builtin_bit_cast(X8, raw);
+}
+
+// LDS fragment reads are issued this many steps ahead of their MFMAs, in a fixed order
+// (sched_barrier between steps): PF1 for the score products, PF2 for the transposed ones.
+// 0: the compiler's order (the hd128 dk/dv kernel has no registers to spare for fragments
+// read ahead: they spill).
+constexpr int BWD_DQ_PF1 = 2, BWD_DQ_PF2 = 2;
+template <int D> constexpr int bwd_kv_pf1() { return D == 128 ? 0 : 2; }
+template <int D> constexpr int bwd_kv_pf2() { return D == 128 ? 0 : 2; }
+
 // Load one BT-row tile of a [.., tokens, heads, D] tensor straight into LDS (padded rows).
 // `base` points at (b, token 0, head); rows past `valid_rows` load zeros.
 template <int D, int NW>
@@ -88,6 +110,7 @@ bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   constexpr int NW = C::NW, BT = C::BT, BR = NW * 32;
   constexpr int KS1 = D / 16, MT2 = D / 32, KS2 = BT / 16, ROW = C::ROW;
+  constexpr int PF1 = BWD_DQ_PF1, PF2 = BWD_DQ_PF2;
   static_assert(BT == 32, "one 32-key score tile per key tile");
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][C::TB], v_lds[2][C::TB];
@@ -156,16 +179,28 @@ bwd_dq_kernel(BwdParams p) {
       const uint8_t* vl = v_lds[buf];
       // S^T and dP^T, each as two alternating accumulators over the head dim
       f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+      {
+        // step t: the K and V fragments of head-dim step t, read PF1 steps ahead
+        x8 kf_[KS1], vf_[KS1];
+        auto rd = [&](const int t) {
+          kf_[t] = __builtin_bit_cast(x8, *(const u32x4*)(kl + k_rd + t * 32));
+          vf_[t] = __builtin_bit_cast(x8, *(const u32x4*)(vl + k_rd + t * 32));
+        };
 #pragma unroll
-      for (int t = 0; t < KS1; t += 2) {
-        const x8 ka = __builtin_bit_cast(x8, *(const u32x4*)(kl + k_rd + t * 32));
-        const x8 kb = __builtin_bit_cast(x8, *(const u32x4*)(kl + k_rd + (t + 1) * 32));
-        const x8 va = __builtin_bit_cast(x8, *(const u32x4*)(vl + k_rd + t * 32));
-        const x8 vb = __builtin_bit_cast(x8, *(const u32x4*)(vl + k_rd + (t + 1) * 32));
-        s0 = T::mfma(ka, qf[t], s0);
-        p0 = T::mfma(va, df[t], p0);
-        s1 = T::mfma(kb, qf[t + 1], s1);
-        p1 = T::mfma(vb, df[t + 1], p1);
+        for (int t = 0; t < PF1; ++t) rd(t);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < KS1; ++t) {
+          if (t + PF1 < KS1) rd(t + PF1);
+          if (t & 1) {
+            s1 = T::mfma(kf_[t], qf[t], s1);
+            p1 = T::mfma(vf_[t], df[t], p1);
+          } else {
+            s0 = T::mfma(kf_[t], qf[t], s0);
+            p0 = T::mfma(vf_[t], df[t], p0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       const f32x16 s = s0 + s1, dp = p0 + p1;
       // P^T, dS^T; key of register r: j*BT + 8(r/4) + 4hh + r%4; query q_lane
@@ -184,20 +219,24 @@ bwd_dq_kernel(BwdParams p) {
         dsf[r >> 3][(r & 7) + 1] = ds[1];
       }
       (void)zero2;
-      // dQ^T += K^T dS^T (K^T read transposed from the K tile)
+      // dQ^T += K^T dS^T (K^T read transposed from the K tile), fragments PF2 steps ahead
+      {
+        constexpr int N = KS2 * MT2;
+        x8 tf[N];
+        auto rd = [&](const int i) {
+          const int u = i / MT2, md = i % MT2;
+          tf[i] = bwd_tr_frag<x8>(kl + t_rd + (16 * u) * ROW + md * 64, ROW);
+        };
 #pragma unroll
-      for (int u = 0; u < KS2; ++u)
+        for (int i = 0; i < PF2; ++i) rd(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int md = 0; md < MT2; ++md) {
-          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kl + t_rd + (16 * u) * ROW + md * 64));
-          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kl + t_rd + (16 * u + 8) * ROW + md * 64));
-          u32x4 raw;
-          raw[0] = __builtin_bit_cast(u32x2, lo4)[0];
-          raw[1] = __builtin_bit_cast(u32x2, lo4)[1];
-          raw[2] = __builtin_bit_cast(u32x2, hi4)[0];
-          raw[3] = __builtin_bit_cast(u32x2, hi4)[1];
-          acc[md] = T::mfma(__builtin_bit_cast(x8, raw), dsf[u], acc[md]);
+        for (int i = 0; i < N; ++i) {
+          if (i + PF2 < N) rd(i + PF2);
+          acc[i % MT2] = T::mfma(tf[i], dsf[i / MT2], acc[i % MT2]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
     }
     __syncthreads();
   }
@@ -230,6 +269,7 @@ bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   constexpr int NW = C::NW, BT = C::BT, BK = NW * 32;
   constexpr int KS1 = D / 16, MT2 = D / 32, KS2 = BT / 16, ROW = C::ROW;
+  constexpr int PF1 = bwd_kv_pf1<D>(), PF2 = bwd_kv_pf2<D>();
   static_assert(BT == 32, "one 32-query score tile per query tile");
 
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[2][C::TB], d_lds[2][C::TB];
@@ -312,16 +352,40 @@ bwd_dkdv_kernel(BwdParams p) {
       const uint8_t* dl = d_lds[buf];
       // S[q][k] and dP[q][k] (A = Q / dO rows from LDS, B = this lane's K / V)
       f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+      if constexpr (PF1 == 0) {
 #pragma unroll
-      for (int t = 0; t < KS1; t += 2) {
-        const x8 qa = __builtin_bit_cast(x8, *(const u32x4*)(ql + a_rd + t * 32));
-        const x8 qb = __builtin_bit_cast(x8, *(const u32x4*)(ql + a_rd + (t + 1) * 32));
-        const x8 da = __builtin_bit_cast(x8, *(const u32x4*)(dl + a_rd + t * 32));
-        const x8 db = __builtin_bit_cast(x8, *(const u32x4*)(dl + a_rd + (t + 1) * 32));
-        s0 = T::mfma(qa, kf[t], s0);
-        p0 = T::mfma(da, vf[t], p0);
-        s1 = T::mfma(qb, kf[t + 1], s1);
-        p1 = T::mfma(db, vf[t + 1], p1);
+        for (int t = 0; t < KS1; t += 2) {
+          const x8 qa = __builtin_bit_cast(x8, *(const u32x4*)(ql + a_rd + t * 32));
+          const x8 qb = __builtin_bit_cast(x8, *(const u32x4*)(ql + a_rd + (t + 1) * 32));
+          const x8 da = __builtin_bit_cast(x8, *(const u32x4*)(dl + a_rd + t * 32));
+          const x8 db = __builtin_bit_cast(x8, *(const u32x4*)(dl + a_rd + (t + 1) * 32));
+          s0 = T::mfma(qa, kf[t], s0);
+          p0 = T::mfma(da, vf[t], p0);
+          s1 = T::mfma(qb, kf[t + 1], s1);
+          p1 = T::mfma(db, vf[t + 1], p1);
+        }
+      } else {
+        // step t: the Q and dO fragments of head-dim step t, read PF1 steps ahead
+        x8 qf_[KS1], df_[KS1];
+        auto rd = [&](const int t) {
+          qf_[t] = __builtin_bit_cast(x8, *(const u32x4*)(ql + a_rd + t * 32));
+          df_[t] = __builtin_bit_cast(x8, *(const u32x4*)(dl + a_rd + t * 32));
+        };
+#pragma unroll
+        for (int t = 0; t < PF1; ++t) rd(t);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < KS1; ++t) {
+          if (t + PF1 < KS1) rd(t + PF1);
+          if (t & 1) {
+            s1 = T::mfma(qf_[t], kf[t], s1);
+            p1 = T::mfma(df_[t], vf[t], p1);
+          } else {
+            s0 = T::mfma(qf_[t], kf[t], s0);
+            p0 = T::mfma(df_[t], vf[t], p0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       const f32x16 s = s0 + s1, dp = p0 + p1;
       // register r holds query q0 + 8(r/4) + 4hh + r%4 of this lane's key k_lane
@@ -355,31 +419,38 @@ bwd_dkdv_kernel(BwdParams p) {
           dsf[r >> 3][(r & 7) + 1] = dd[1];
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T read transposed from the tiles)
+      // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T read transposed from the tiles),
+      // fragments PF2 steps ahead
+      if constexpr (PF2 == 0) {
 #pragma unroll
-      for (int u = 0; u < KS2; ++u)
+        for (int u = 0; u < KS2; ++u)
 #pragma unroll
-        for (int md = 0; md < MT2; ++md) {
-          u32x4 rq, rd;
-          {
-            const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(dl + t_rd + (16 * u) * ROW + md * 64));
-            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(dl + t_rd + (16 * u + 8) * ROW + md * 64));
-            rd[0] = __builtin_bit_cast(u32x2, lo4)[0];
-            rd[1] = __builtin_bit_cast(u32x2, lo4)[1];
-            rd[2] = __builtin_bit_cast(u32x2, hi4)[0];
-            rd[3] = __builtin_bit_cast(u32x2, hi4)[1];
+          for (int md = 0; md < MT2; ++md) {
+            const x8 rdo = bwd_tr_frag<x8>(dl + t_rd + (16 * u) * ROW + md * 64, ROW);
+            const x8 rq = bwd_tr_frag<x8>(ql + t_rd + (16 * u) * ROW + md * 64, ROW);
+            dv[md] = T::mfma(rdo, pf[u], dv[md]);
+            dk[md] = T::mfma(rq, dsf[u], dk[md]);
           }
-          {
-            const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ql + t_rd + (16 * u) * ROW + md * 64));
-            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ql + t_rd + (16 * u + 8) * ROW + md * 64));
-            rq[0] = __builtin_bit_cast(u32x2, lo4)[0];
-            rq[1] = __builtin_bit_cast(u32x2, lo4)[1];
-            rq[2] = __builtin_bit_cast(u32x2, hi4)[0];
-            rq[3] = __builtin_bit_cast(u32x2, hi4)[1];
-          }
-          dv[md] = T::mfma(__builtin_bit_cast(x8, rd), pf[u], dv[md]);
-          dk[md] = T::mfma(__builtin_bit_cast(x8, rq), dsf[u], dk[md]);
+      } else {
+        constexpr int N = KS2 * MT2;
+        x8 tdf[N], tqf[N];
+        auto rd = [&](const int i) {
+          const int u = i / MT2, md = i % MT2;
+          tdf[i] = bwd_tr_frag<x8>(dl + t_rd + (16 * u) * ROW + md * 64, ROW);
+          tqf[i] = bwd_tr_frag<x8>(ql + t_rd + (16 * u) * ROW + md * 64, ROW);
+        };
+#pragma unroll
+        for (int i = 0; i < PF2; ++i) rd(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          if (i + PF2 < N) rd(i + PF2);
+          const int u = i / MT2, md = i % MT2;
+          dv[md] = T::mfma(tdf[i], pf[u], dv[md]);
+          dk[md] = T::mfma(tqf[i], dsf[u], dk[md]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
     }
     __syncthreads();
   }
