@@ -67,11 +67,13 @@ def _bound(qd, kd, vd, o_ref, causal, scale, rows, hkv_of):
     return out, sd
 
 
-def _run(name, B, N, Hq, Hkv, d, causal, seed, rows=None):
-    q, k, v = W.make_qkv(B, N, N, Hq, Hkv, d, seed, dtype=torch.float32)
+def _run(name, B, N, Hq, Hkv, d, causal, seed, rows=None, Nk=None, scale=None):
+    Nk = N if Nk is None else Nk
+    q, k, v = W.make_qkv(B, N, Nk, Hq, Hkv, d, seed, dtype=torch.float32)
     (q8, qs), (k8, ks), (v8, vs) = _quant(q), _quant(k), _quant(v)
-    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
-    _say(f"[gpu] fp8 {name} B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed={seed}")
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    _say(f"[gpu] fp8 {name} B={B} Nq={N} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} scale={scale} seed={seed}")
     o, lse = fa.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), qs, ks, vs, causal=causal, scale=scale)
     torch.cuda.synchronize()
     qd = q8.double().numpy() * qs
@@ -124,6 +126,27 @@ def test_fp8_full_size_sampled_rows(wname, causal):
     w = W.by_name(wname)
     rows = [0, 1, 63, 64, 127, 128, 4095, 4096, w.N - 2, w.N - 1] + list(range(200, 8000, 1201))
     _run(wname, w.B, w.N, w.Hq, w.Hkv, w.d, causal, w.seed, rows=rows)
+
+
+RECT = [
+    # name,        Nq,  Nk,  Hq, Hkv, d,  seed
+    ("q_short",    70,  900, 2,  1,  128, 108),
+    ("q_long",     300, 65,  4,  4,  256, 109),
+    ("k_single",   129, 1,   2,  1,  128, 110),
+]
+
+
+@pytest.mark.parametrize("case", RECT, ids=[c[0] for c in RECT])
+def test_fp8_rectangular_noncausal(case):
+    name, Nq, Nk, Hq, Hkv, d, seed = case
+    _run(name, 1, Nq, Hq, Hkv, d, False, seed, Nk=Nk)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_fp8_zero_scale(d, causal):
+    # every visible key gets weight 1 exactly (in e4m3 too): O = mean of the visible V rows
+    _run(f"zero_scale_d{d}", 1, 257, 2, 1, d, causal, 111 + d, scale=0.0)
 
 
 def test_fp8_scales_enter_exactly():
