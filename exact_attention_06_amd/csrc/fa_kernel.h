@@ -21,10 +21,13 @@
 //     the 16-byte K reads of 16 consecutive rows and the transpose reads of V (two 16-lane
 //     groups, 4 rows x 32 B each) hit distinct banks, and every LDS read address is one
 //     per-lane base plus an immediate;
-//   * software pipeline inside each wave: while the softmax of tile j runs on the VALU,
-//     the score MFMAs of tile j+1 are in flight; then the P.V MFMAs of tile j. K(j+2) and
-//     V(j+1) are loaded at the top of iteration j by buffer loads that write LDS directly
-//     (no staging registers) and whose range check returns zeros past the last key;
+//   * two loop schedules (LoopMode below). PIPE (hd128): a software pipeline inside each
+//     wave - while the softmax of tile j runs on the VALU, the score MFMAs of tile j+1 are
+//     in flight; then the P.V MFMAs of tile j; K(j+2) and V(j+1) are loaded at the top of
+//     iteration j. SEQ (hd256): one tile at a time, two workgroups per CU overlapping each
+//     other, LDS fragments read four MFMAs ahead; K(j+1) and V(j+1) are loaded at the top of
+//     iteration j. Tile loads are buffer loads that write LDS directly (no staging
+//     registers) and whose range check returns zeros past the last key;
 //   * softmax in base 2: p = exp2(s*c - m), c = scale*log2(e), on v_exp_f32;
 //   * lazy rescale: the running max m (log2 units) is raised only when some row of the
 //     wave sees a tile max above m + TAU; until then p <= 2^TAU;
