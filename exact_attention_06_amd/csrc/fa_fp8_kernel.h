@@ -4,8 +4,9 @@
 // table of section "Phase 2": FP8 input on the FP8 tensor-core MMA). The caller passes
 // e4m3 tensors and one dequantisation factor per tensor (q_scale, k_scale, v_scale); the
 // operation is the dense one of fa_fwd on the dequantised values. Both products run on
-// v_mfma_f32_32x32x64_f8f6f4 (fp8 x fp8 -> fp32, twice the bf16 rate): S^T = K Q^T exactly
-// (fp8 products are exact in fp32), and O^T += V^T P^T with P rounded to e4m3. The row sum
+// v_mfma_f32_32x32x64_f8f6f4 (fp8 x fp8 -> fp32, twice the bf16 rate): S^T = K Q^T (the
+// products are exact; the MFMA sums each group of 64 with fewer bits than fp32, measured at
+// up to ~2^-14 of sum |q k|), and O^T += V^T P^T with P rounded to e4m3. The row sum
 // that normalises O is the fp32 sum of the rounded P (one extra MFMA against an all-ones
 // operand), so P's rounding largely cancels in O; the LSE uses the fp32 sum of unrounded p.
 //

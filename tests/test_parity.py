@@ -146,6 +146,14 @@ def test_zero_scale(d, causal):
     _run_full(f"zero_scale_d{d}", 1, 257, 257, 2, 1, d, causal, 70 + d, scale=0.0)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_hot_scores(d, causal):
+    # scale 1 instead of 1/sqrt(d): scores with a spread of about sqrt(d) make nearly one-hot
+    # rows whose running max keeps jumping by far more than the rescale threshold
+    _run_full(f"hot_scores_d{d}", 1, 600, 600, 2, 1, d, causal, 80 + d, scale=1.0)
+
+
 @pytest.mark.parametrize("w", [W.tiny(), W.ragged()], ids=["tiny", "ragged"])
 def test_named_small_workloads(w):
     for causal in w.causal_modes:
