@@ -167,7 +167,6 @@ bwd_dq_kernel(BwdParams p) {
   bwd_load_rows<D, NW>(kbase, kv_row, 0, Nk, k_lds[0], wv, lane);
   bwd_load_rows<D, NW>(vbase, kv_row, 0, Nk, v_lds[0], wv, lane);
   __syncthreads();
-  const x2 zero2 = T::cvt2(0.f, 0.f);
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
     if (j + 1 < ntiles) {
@@ -218,7 +217,6 @@ bwd_dq_kernel(BwdParams p) {
         dsf[r >> 3][r & 7] = ds[0];
         dsf[r >> 3][(r & 7) + 1] = ds[1];
       }
-      (void)zero2;
       // dQ^T += K^T dS^T (K^T read transposed from the K tile), fragments PF2 steps ahead
       {
         constexpr int N = KS2 * MT2;
