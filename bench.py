@@ -135,7 +135,9 @@ def cpu_baseline(w, causal, budget_s=12.0):
                       f"{dt:.1f} s of CPU work; FLOPs 4*d per visible key per row"}
 
 
-def load_traffic(kernel_name):
+def load_profile(kernel_name):
+    """The committed rocprofv3 record of this kernel (profiles/traffic.json), or None when the
+    kernel sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -143,7 +145,12 @@ def load_traffic(kernel_name):
     e = rec.get(kernel_name)
     if not e or e.get("source_hash") != kernel_source_hash():
         return None
-    return e.get("hbm_bytes_per_launch")
+    return e
+
+
+def load_traffic(kernel_name):
+    e = load_profile(kernel_name)
+    return None if e is None else e.get("hbm_bytes_per_launch")
 
 
 def main():
@@ -360,6 +367,12 @@ def main():
         log(f"[cpu] oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['sample']})")
 
     kname = f"fwd_kernel<{w.d},{'causal' if causal else 'noncausal'},bf16>"
+    # counter figures from the same committed profile as `traffic` (null when stale): the shader
+    # clock the kernel ran at and its MFMA/VALU busy fractions
+    prof = load_profile(kname)
+    counters = None if prof is None or "sclk_ghz" not in prof else {
+        "sclk_ghz": prof["sclk_ghz"], "mfma_busy": prof["mfma_busy"], "valu_busy": prof["valu_busy"],
+        "source": "profiles/traffic.json (rocprofv3 SQ counters)"}
     b200 = PAGES_B200.get((w.name, causal))
     rec = {
         "metric": "fwd attention TFLOPS + % of MI355X bf16 MFMA peak, hd128/hd256 at N=1k-128k",
@@ -380,6 +393,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": load_traffic(kname), "kernel": kname,
+                     "counters": counters,
                      "avg_launch_ms": round(avg_launch_ms, 4),
                      "flops_per_launch": flops},
         "cpu_baseline": cpu,
