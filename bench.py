@@ -211,10 +211,10 @@ def main():
 
     sweep = []
     if not args.no_sweep:
-        pts = [x for x in W.hd128_sweep() + W.hd256_sweep() + W.hd512_sweep()]
+        pts = [x for x in W.hd128_sweep() + W.hd256_sweep() + [W.video()] + W.hd512_sweep()]
         for x in pts:
             qx, kx, vx = gpu_inputs(x, torch)
-            for c in (False, True):
+            for c in x.causal_modes:
                 m, _ = time_forward(fa, torch, qx, kx, vx, c, x.scale, args.sweep_steps, 2)
                 t = x.flops(c) / (m * 1e-3) / 1e12
                 ent = {"workload": x.name, "causal": c, "B": x.B, "N": x.N, "Hq": x.Hq, "Hkv": x.Hkv,
