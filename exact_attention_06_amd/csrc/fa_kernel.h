@@ -229,9 +229,16 @@ fwd_kernel(FwdParams p) {
 
   // Two K and two V tile buffers as separate LDS objects: the loop's buffer parity is a
   // compile-time value, so the compiler can see that the direct-to-LDS loads of the next
-  // tiles never touch the buffers being read and does not wait for them early.
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds0[L::KBUF], k_lds1[L::KBUF], v_lds0[L::VBUF],
-      v_lds1[L::VBUF];
+  // tiles never touch the buffers being read and does not wait for them early. The compiler
+  // lays the objects out in the order of their names; the V buffers come first so that every
+  // V transpose read (the most frequent LDS read) is a base register plus an immediate below
+  // 64 KB, with no address add in the loop (hd128: -17 VALU ops per tile, +1.5-4%).
+  __shared__ __attribute__((aligned(16))) uint8_t lds0_v[L::VBUF], lds1_v[L::VBUF], lds2_k[L::KBUF],
+      lds3_k[L::KBUF];
+  uint8_t* const v_lds0 = lds0_v;
+  uint8_t* const v_lds1 = lds1_v;
+  uint8_t* const k_lds0 = lds2_k;
+  uint8_t* const k_lds1 = lds3_k;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
