@@ -203,6 +203,7 @@ def main():
     flops = w.flops(causal)
     tflops = flops / (ms * 1e-3) / 1e12
     avg_launch_ms = sum(per) / len(per)
+    median_launch_ms = sorted(per)[len(per) // 2]
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     del q, k, v
     torch.cuda.empty_cache()
@@ -395,6 +396,7 @@ def main():
                      "traffic": load_traffic(kname), "kernel": kname,
                      "counters": counters,
                      "avg_launch_ms": round(avg_launch_ms, 4),
+                     "median_launch_ms": round(median_launch_ms, 4),
                      "flops_per_launch": flops},
         "cpu_baseline": cpu,
         "sweep": sweep,
