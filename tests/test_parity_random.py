@@ -1,0 +1,55 @@
+"""GPU parity on seeded random shapes: batch, lengths (rectangular when non-causal), GQA ratio,
+head dim, element type and mask drawn per case, every row compared with the fp64 oracle at the
+dense path's tolerance (O max-abs <= 1e-2, mean-abs <= 1e-3, LSE max-abs <= 1e-3; elements with
+|O_ref| >= 4 as in test_parity.py)."""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_06_amd as fa
+from exact_attention_06_amd import workloads as W
+from oracle import attention_ref
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_MAX = 1e-2, 1e-3, 1e-3
+EXCESS = O_MAX - 2.0 ** -7
+
+
+def _case(i):
+    g = np.random.default_rng(1000 + i)
+    d = int(g.choice([128, 256, 512]))
+    hkv = int(g.choice([1, 2, 4]))
+    hq = hkv * int(g.choice([1, 2, 4]))
+    causal = bool(g.integers(0, 2))
+    nq = int(g.integers(1, 700))
+    nk = nq if causal else int(g.integers(1, 700))
+    b = int(g.integers(1, 4))
+    dtype = torch.bfloat16 if g.integers(0, 3) else torch.float16
+    return dict(B=b, Nq=nq, Nk=nk, Hq=hq, Hkv=hkv, d=d, causal=causal, dtype=dtype, seed=2000 + i)
+
+
+CASES = [_case(i) for i in range(30)]
+
+
+@pytest.mark.parametrize("c", CASES, ids=[f"case{i}" for i in range(len(CASES))])
+def test_random_shape(c):
+    q, k, v = W.make_qkv(c["B"], c["Nq"], c["Nk"], c["Hq"], c["Hkv"], c["d"], c["seed"], dtype=c["dtype"])
+    scale = float(torch.tensor(c["d"] ** -0.5, dtype=torch.float32))
+    print(f"[gpu] random {c}", flush=True)
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=c["causal"], scale=scale)
+    torch.cuda.synchronize()
+    O_ref, L_ref = attention_ref(q, k, v, c["causal"], scale)
+    og = o.float().cpu().numpy().astype(np.float64)
+    lg = lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    mant = 7 if c["dtype"] == torch.bfloat16 else 10
+    eo = np.abs(og - O_ref)
+    big = np.abs(O_ref) >= 4.0
+    half_ulp = 0.5 * np.exp2(np.floor(np.log2(np.maximum(np.abs(O_ref), 2.0 ** -126))) - mant)
+    mx_small = float(eo[~big].max()) if (~big).any() else 0.0
+    ex_big = float((eo - half_ulp)[big].max()) if big.any() else 0.0
+    lmx = float(np.abs(lg - L_ref).max())
+    print(f"  O max {eo.max():.3e} mean {eo.mean():.3e} LSE max {lmx:.3e}", flush=True)
+    assert mx_small <= O_MAX and ex_big <= EXCESS and eo.mean() <= O_MEAN and lmx <= LSE_MAX
