@@ -146,3 +146,45 @@ def test_var_workloads(w):
             _run_paged(w.name, w.seqlens_q, w.seqlens_k, w.page_size, w.Hq, w.Hkv, w.d, causal, w.seed)
         else:
             _run_varlen(w.name, w.seqlens_q, w.seqlens_k, w.Hq, w.Hkv, w.d, causal, w.seed)
+
+
+# ---------------------------------------------------------------- seeded random batches
+
+def _random_varlen(i):
+    g = np.random.default_rng(3000 + i)
+    B = int(g.integers(1, 7))
+    Lq = [int(x) for x in g.integers(0, 400, B)]
+    if sum(Lq) == 0:
+        Lq[0] = 1
+    causal = bool(g.integers(0, 2))
+    Lk = [int(x) for x in g.integers(0, 900, B)]
+    used = [int(g.integers(0, n + 1)) for n in Lk] if g.integers(0, 2) else None
+    hkv = int(g.choice([1, 2, 4]))
+    return (f"rv{i}", tuple(Lq), tuple(Lk), hkv * int(g.choice([1, 2])), hkv, int(g.choice([128, 256])), causal,
+            4000 + i, None if used is None else tuple(used))
+
+
+def _random_paged(i):
+    g = np.random.default_rng(5000 + i)
+    B = int(g.integers(1, 7))
+    Lq = tuple(int(x) for x in g.integers(1, 200, B))
+    used = tuple(int(x) for x in g.integers(0, 1500, B))
+    hkv = int(g.choice([1, 2, 4]))
+    return (f"rp{i}", Lq, used, int(g.choice([64, 128, 192, 256])), hkv * int(g.choice([1, 2])), hkv,
+            int(g.choice([128, 256])), bool(g.integers(0, 2)), 6000 + i)
+
+
+RV = [_random_varlen(i) for i in range(12)]
+RP = [_random_paged(i) for i in range(12)]
+
+
+@pytest.mark.parametrize("case", RV, ids=[c[0] for c in RV])
+def test_random_varlen(case):
+    name, Lq, Lk, Hq, Hkv, d, causal, seed, used = case
+    _run_varlen(name, Lq, Lk, Hq, Hkv, d, causal, seed, used)
+
+
+@pytest.mark.parametrize("case", RP, ids=[c[0] for c in RP])
+def test_random_paged(case):
+    name, Lq, used, page, Hq, Hkv, d, causal, seed = case
+    _run_paged(name, Lq, used, page, Hq, Hkv, d, causal, seed)
