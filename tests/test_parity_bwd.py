@@ -104,3 +104,24 @@ FULL_BWD = [W.by_name(n) for n in ("hd128_N8192_mha", "hd128_N8192_gqa4", "hd256
 def test_bwd_full_size_one_head(w, causal):
     # full-size launch; the oracle covers KV head 0 of the last batch (and its query heads)
     _run(w.name, w.B, w.N, w.N, w.Hq, w.Hkv, w.d, causal, w.seed, head=(w.B - 1, 0))
+
+
+def _random_case(i):
+    g = np.random.default_rng(7000 + i)
+    d = int(g.choice([128, 256]))
+    hkv = int(g.choice([1, 2]))
+    hq = hkv * int(g.choice([1, 2, 4]))
+    causal = bool(g.integers(0, 2))
+    nq = int(g.integers(1, 400))
+    nk = nq if causal else int(g.integers(1, 400))
+    dtype = torch.bfloat16 if g.integers(0, 3) else torch.float16
+    return (f"rb{i}", int(g.integers(1, 3)), nq, nk, hq, hkv, d, causal, 8000 + i, dtype)
+
+
+RB = [_random_case(i) for i in range(12)]
+
+
+@pytest.mark.parametrize("case", RB, ids=[c[0] for c in RB])
+def test_bwd_random_shape(case):
+    name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype = case
+    _run(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=dtype)
