@@ -328,39 +328,46 @@ def main():
             del q8, k8, v8
             torch.cuda.empty_cache()
 
-    # serving variants: packed variable-length prefill, paged prefill, paged decode
+    # serving variants: packed variable-length prefill, paged prefill, paged decode; each without
+    # splits and, where the library picks a split count for its shape, split over the keys too
     variants = []
     if not args.no_sweep:
         for x in W.bench_var_workloads():
+            mq = max(x.seqlens_q)
             if x.paged:
                 qx, kc, vc, cu, used, bt = (t.cuda() for t in W.var_inputs(x, device="cuda"))
-                call = lambda c: fa.forward_paged(qx, kc, vc, cu, used, bt, max(x.seqlens_q), causal=c,
-                                                  scale=x.scale)
+                bound = bt.shape[1] * kc.shape[1]
+                call = lambda c, ns: fa.forward_paged(qx, kc, vc, cu, used, bt, mq, causal=c, scale=x.scale,
+                                                      num_splits=ns)
             else:
                 qx, kx, vx, cu, cuk = (t.cuda() for t in W.var_inputs(x, device="cuda"))
-                call = lambda c: fa.forward_varlen(qx, kx, vx, cu, cuk, max(x.seqlens_q), causal=c,
-                                                   scale=x.scale)
+                bound = kx.shape[0]
+                call = lambda c, ns: fa.forward_varlen(qx, kx, vx, cu, cuk, mq, causal=c, scale=x.scale,
+                                                       num_splits=ns)
+            ns_lib = fa.var_num_splits(x.B, mq, bound, x.Hq, x.d)
             for c in x.causal_modes:
-                for _ in range(2):
-                    call(c)
-                torch.cuda.synchronize()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                n = max(1, args.sweep_steps)
-                e0.record()
-                for _ in range(n):
-                    call(c)
-                e1.record()
-                torch.cuda.synchronize()
-                m = e0.elapsed_time(e1) / n
-                t = x.flops(c) / (m * 1e-3) / 1e12
-                kv_bytes = 2 * 2 * x.Hkv * x.d * sum(x.seqlens_k)  # K and V rows used, bf16
-                ent = {"workload": x.name, "causal": c, "B": x.B, "total_q": sum(x.seqlens_q),
-                       "total_k": sum(x.seqlens_k), "Hq": x.Hq, "Hkv": x.Hkv, "d": x.d, "paged": x.paged,
-                       "ms": round(m, 4), "tflops": round(t, 1), "kv_gbps": round(kv_bytes / (m * 1e-3) / 1e9, 1)}
-                variants.append(ent)
-                log(f"[var] {x.name:26s} {'causal' if c else 'noncausal':9s} {m:8.3f} ms {t:7.1f} TFLOPS "
-                    f"K/V {ent['kv_gbps']:7.1f} GB/s")
+                for ns in [0] + ([ns_lib] if ns_lib else []):
+                    for _ in range(2):
+                        call(c, ns)
+                    torch.cuda.synchronize()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    n = max(1, args.sweep_steps)
+                    e0.record()
+                    for _ in range(n):
+                        call(c, ns)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    m = e0.elapsed_time(e1) / n
+                    t = x.flops(c) / (m * 1e-3) / 1e12
+                    kv_bytes = 2 * 2 * x.Hkv * x.d * sum(x.seqlens_k)  # K and V rows used, bf16
+                    ent = {"workload": x.name, "causal": c, "B": x.B, "total_q": sum(x.seqlens_q),
+                           "total_k": sum(x.seqlens_k), "Hq": x.Hq, "Hkv": x.Hkv, "d": x.d, "paged": x.paged,
+                           "num_splits": ns, "ms": round(m, 4), "tflops": round(t, 1),
+                           "kv_gbps": round(kv_bytes / (m * 1e-3) / 1e9, 1)}
+                    variants.append(ent)
+                    log(f"[var] {x.name:26s} {'causal' if c else 'noncausal':9s} splits {ns:2d} {m:8.3f} ms "
+                        f"{t:7.1f} TFLOPS K/V {ent['kv_gbps']:7.1f} GB/s")
             torch.cuda.empty_cache()
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, causal)

@@ -24,7 +24,7 @@ import math
 from . import _lib
 
 __all__ = ["forward", "forward_fp8", "forward_splitkv", "num_splits", "backward", "forward_varlen",
-           "forward_paged", "check_args", "FaError"]
+           "forward_paged", "var_num_splits", "check_args", "FaError"]
 
 
 class FaError(ValueError):
@@ -258,15 +258,33 @@ def _varlen_out(q, out, lse, torch):
     return out, lse
 
 
+def var_num_splits(B: int, max_seqlen_q: int, key_bound: int, Hq: int, d: int) -> int:
+    """The library's split count for a variable-length / paged batch (fa_fwd_var_num_splits);
+    key_bound bounds every sequence's key count (paged: max_pages * page_size). 0: no split."""
+    return int(_lib.load().fa_fwd_var_num_splits(B, max_seqlen_q, key_bound, Hq, d))
+
+
+def _var_workspace(lib, total_q, Hq, d, num_splits, q, torch):
+    nbytes = lib.fa_fwd_var_splitkv_workspace_bytes(total_q, Hq, d, int(num_splits))
+    if nbytes == 0:
+        raise ValueError("num_splits must be a positive integer")
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=q.device), nbytes
+
+
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
-                   scale: float | None = None, seqused_k=None, out=None, lse=None):
+                   scale: float | None = None, seqused_k=None, out=None, lse=None, num_splits: int = 0):
     """Packed variable-length forward (fa_fwd_varlen): q [total_q, Hq, d], k/v [total_k, Hkv, d],
     cu_seqlens_q / cu_seqlens_k int32 [B+1], seqused_k None or int32 [B]. Returns
-    o [total_q, Hq, d] and lse [Hq, total_q] (fp32)."""
+    o [total_q, Hq, d] and lse [Hq, total_q] (fp32). num_splits > 0 cuts every sequence's keys
+    into chunks over that many split-KV blocks (fa_fwd_varlen_splitkv; workspace allocated here)."""
     import torch
 
     lib = _lib.load()
-    fn = _varlen_common(q, (("k", k), ("v", v)), torch, lib, "fa_fwd_varlen", "fa_fwd_varlen_f16")
+    if num_splits:
+        fn = _varlen_common(q, (("k", k), ("v", v)), torch, lib, "fa_fwd_varlen_splitkv",
+                            "fa_fwd_varlen_splitkv_f16")
+    else:
+        fn = _varlen_common(q, (("k", k), ("v", v)), torch, lib, "fa_fwd_varlen", "fa_fwd_varlen_f16")
     if q.dim() != 3 or k.dim() != 3 or tuple(v.shape) != tuple(k.shape) or k.shape[2] != q.shape[2]:
         raise ValueError("q must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
     total_q, Hq, d = q.shape
@@ -281,26 +299,37 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causa
     out, lse = _varlen_out(q, out, lse, torch)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
-                0 if seqused_k is None else seqused_k.data_ptr(), B, int(max_seqlen_q), total_q, total_k,
-                Hq, Hkv, d, int(bool(causal)), float(scale), stream)
+        used = 0 if seqused_k is None else seqused_k.data_ptr()
+        if num_splits:
+            ws, nbytes = _var_workspace(lib, total_q, Hq, d, num_splits, q, torch)
+            rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), ws.data_ptr(), nbytes,
+                    cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), used, B, int(max_seqlen_q), total_q, total_k,
+                    Hq, Hkv, d, int(bool(causal)), float(scale), int(num_splits), stream)
+        else:
+            rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), used, B, int(max_seqlen_q), total_q, total_k,
+                    Hq, Hkv, d, int(bool(causal)), float(scale), stream)
     if rc != 0:
         _raise(rc)
     return out, lse
 
 
 def forward_paged(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table, max_seqlen_q: int,
-                  causal: bool = False, scale: float | None = None, out=None, lse=None):
+                  causal: bool = False, scale: float | None = None, out=None, lse=None, num_splits: int = 0):
     """Forward against a paged K/V cache (fa_fwd_paged): q [total_q, Hq, d],
     k_cache/v_cache [num_pages, page_size, Hkv, d], cu_seqlens_q int32 [B+1], seqused_k
     int32 [B], block_table int32 [B, max_pages]. Returns o [total_q, Hq, d] and
-    lse [Hq, total_q] (fp32)."""
+    lse [Hq, total_q] (fp32). num_splits > 0 cuts every sequence's keys into chunks over that
+    many split-KV blocks (fa_fwd_paged_splitkv; workspace allocated here)."""
     import torch
 
     lib = _lib.load()
-    fn = _varlen_common(q, (("k_cache", k_cache), ("v_cache", v_cache)), torch, lib, "fa_fwd_paged",
-                        "fa_fwd_paged_f16")
+    if num_splits:
+        fn = _varlen_common(q, (("k_cache", k_cache), ("v_cache", v_cache)), torch, lib, "fa_fwd_paged_splitkv",
+                            "fa_fwd_paged_splitkv_f16")
+    else:
+        fn = _varlen_common(q, (("k_cache", k_cache), ("v_cache", v_cache)), torch, lib, "fa_fwd_paged",
+                            "fa_fwd_paged_f16")
     if (q.dim() != 3 or k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape)
             or k_cache.shape[3] != q.shape[2]):
         raise ValueError("q must be [total_q, Hq, d] and k_cache, v_cache [num_pages, page_size, Hkv, d]")
@@ -319,10 +348,17 @@ def forward_paged(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table, max
     out, lse = _varlen_out(q, out, lse, torch)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                cu_seqlens_q.data_ptr(), seqused_k.data_ptr(), block_table.data_ptr(), B, int(max_seqlen_q),
-                total_q, num_pages, page_size, block_table.shape[1], Hq, Hkv, d, int(bool(causal)),
-                float(scale), stream)
+        if num_splits:
+            ws, nbytes = _var_workspace(lib, total_q, Hq, d, num_splits, q, torch)
+            rc = fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    ws.data_ptr(), nbytes, cu_seqlens_q.data_ptr(), seqused_k.data_ptr(), block_table.data_ptr(), B,
+                    int(max_seqlen_q), total_q, num_pages, page_size, block_table.shape[1], Hq, Hkv, d,
+                    int(bool(causal)), float(scale), int(num_splits), stream)
+        else:
+            rc = fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    cu_seqlens_q.data_ptr(), seqused_k.data_ptr(), block_table.data_ptr(), B, int(max_seqlen_q),
+                    total_q, num_pages, page_size, block_table.shape[1], Hq, Hkv, d, int(bool(causal)),
+                    float(scale), stream)
     if rc != 0:
         _raise(rc)
     return out, lse

@@ -41,6 +41,14 @@ _PAGED_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _
 _SPLIT_ARGS = [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P]
 _BWD_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _I, _I, _I,
              ctypes.c_float, _P]
+# q, k, v, o, lse, workspace, workspace_bytes, cu_q, cu_k, seqused, B, max_seqlen_q, total_q,
+# total_k, Hq, Hkv, d, causal, scale, num_splits, stream
+_VARLEN_SPLIT_ARGS = [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                      ctypes.c_float, _I, _P]
+# q, kc, vc, o, lse, workspace, workspace_bytes, cu_q, seqused, block_table, B, max_seqlen_q,
+# total_q, num_pages, page_size, max_pages, Hq, Hkv, d, causal, scale, num_splits, stream
+_PAGED_SPLIT_ARGS = [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                     _I, ctypes.c_float, _I, _P]
 
 
 def load():
@@ -67,6 +75,18 @@ def load():
             fn = getattr(lib, name)
             fn.argtypes = _SPLIT_ARGS
             fn.restype = _I
+        for name in ("fa_fwd_varlen_splitkv", "fa_fwd_varlen_splitkv_f16"):
+            fn = getattr(lib, name)
+            fn.argtypes = _VARLEN_SPLIT_ARGS
+            fn.restype = _I
+        for name in ("fa_fwd_paged_splitkv", "fa_fwd_paged_splitkv_f16"):
+            fn = getattr(lib, name)
+            fn.argtypes = _PAGED_SPLIT_ARGS
+            fn.restype = _I
+        lib.fa_fwd_var_num_splits.argtypes = [_I, _I, _I, _I, _I]
+        lib.fa_fwd_var_num_splits.restype = _I
+        lib.fa_fwd_var_splitkv_workspace_bytes.argtypes = [_I, _I, _I, _I]
+        lib.fa_fwd_var_splitkv_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_splitkv_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_num_splits.argtypes = [_I, _I, _I, _I, _I, _I]

@@ -28,6 +28,12 @@ int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
     hipLaunchKernelGGL((fa::fwd_combine<D, T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, prm);
     if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   }
+  if (VM == 3) {  // variable-length split-KV: merge the partials of the packed rows
+    const size_t threads = (size_t)prm.Hq * prm.total_q * (D / 8);
+    hipLaunchKernelGGL((fa::fwd_combine_var<D, T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       prm);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  }
   return FA_OK;
 }
 
@@ -42,7 +48,7 @@ template <int VM, class T>
 int dispatch(fa::FwdParams& prm, int d, int causal, hipStream_t s) {
   const int BR = d == 128 ? fa::Layout<128>::BR : fa::Layout<256>::BR;
   prm.nqt = (prm.Nq + BR - 1) / BR;
-  const int grid = prm.B * prm.Hq * prm.nqt * (VM == 2 ? prm.splits : 1);
+  const int grid = prm.B * prm.Hq * prm.nqt * (VM >= 2 ? prm.splits : 1);
   if (d == 128)
     return causal ? launch<128, true, T, VM>(prm, grid, s) : launch<128, false, T, VM>(prm, grid, s);
   return causal ? launch<256, true, T, VM>(prm, grid, s) : launch<256, false, T, VM>(prm, grid, s);
@@ -239,14 +245,47 @@ int check_var(const void* q, const void* k, const void* v, const void* o, const 
   return FA_OK;
 }
 
+size_t var_splitkv_ws_bytes(int total_q, int Hq, int d, int splits) {
+  if (total_q <= 0 || Hq <= 0 || (d != 128 && d != 256) || splits < 1) return 0;
+  return (size_t)splits * Hq * total_q * (size_t)(d + 1) * sizeof(float);
+}
+
+// Split count for variable-length / paged batches, measured on MI355X (128 paged sequences of
+// 1k..32k keys, 1..16 queries each, hd256: 4.2 TB/s of K/V without splits, 5.5-5.8 TB/s with
+// 2..16, best at 8; packed and paged prefill of 32k tokens only get slower, by the partials'
+// traffic): split decode-shaped batches (at most 64 query rows per sequence) whose key bound
+// spans many tiles.
+int var_num_splits(int B, int max_seqlen_q, int key_bound, int Hq, int d) {
+  if (B <= 0 || max_seqlen_q <= 0 || key_bound <= 0 || Hq <= 0 || (d != 128 && d != 256)) return 0;
+  if (max_seqlen_q > 64) return 0;
+  const int tiles = (key_bound + key_tile(d) - 1) / key_tile(d);
+  if (tiles < 32) return 0;
+  return tiles >= 128 ? 8 : std::max(2, tiles / 16);
+}
+
+// splits = 0: no split. Otherwise every sequence's key tiles are cut into chunks of tps tiles,
+// tps = ceil(ceil(K / BC) / splits) for K a bound on any sequence's key count (paged:
+// max_pages * page_size; packed: total_k), so that the splits cover every sequence's keys.
 template <class T>
 int run_var(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_q,
             const int* cu_k, const int* seqused, const int* block_table, int B, int max_seqlen_q,
             int total_q, int total_k, int num_pages, int page_size, int max_pages, int Hq, int Hkv,
-            int d, int causal, float scale, void* stream, bool paged) {
+            int d, int causal, float scale, void* stream, bool paged, int splits = 0, void* ws = nullptr,
+            size_t ws_bytes = 0) {
   const int st = check_var(q, k, v, o, lse, cu_q, cu_k, seqused, block_table, B, max_seqlen_q, total_q,
                            total_k, num_pages, page_size, max_pages, Hq, Hkv, d, scale, paged);
   if (st != FA_OK) return st;
+  int tps = 0;
+  if (splits != 0) {
+    if (splits < 1 || splits > 256) return FA_ERR_SHAPE;
+    if (!ws || ws_bytes < var_splitkv_ws_bytes(total_q, Hq, d, splits) || ((uintptr_t)ws & 15))
+      return FA_ERR_WORKSPACE;
+    const int64_t BR = d == 128 ? br<128>() : br<256>();
+    if ((int64_t)B * Hq * ((max_seqlen_q + BR - 1) / BR) * splits > INT_MAX) return FA_ERR_TOO_LARGE;
+    const int64_t bound = paged ? (int64_t)max_pages * page_size : (int64_t)total_k;
+    const int64_t tiles = (bound + key_tile(d) - 1) / key_tile(d);
+    tps = (int)std::max<int64_t>(1, (tiles + splits - 1) / splits);
+  }
   fa::FwdParams prm;
   prm.q = (const uint8_t*)q;
   prm.k = (const uint8_t*)k;
@@ -270,8 +309,14 @@ int run_var(const void* q, const void* k, const void* v, void* o, float* lse, co
   prm.num_pages = paged ? num_pages : 0;
   prm.part_o = prm.part_lse = nullptr;
   prm.splits = prm.tps = 0;
+  prm.v_scale = 1.f;
   set_scale(prm, scale);
-  return dispatch<1, T>(prm, d, causal, (hipStream_t)stream);
+  if (splits == 0) return dispatch<1, T>(prm, d, causal, (hipStream_t)stream);
+  prm.splits = splits;
+  prm.tps = tps;
+  prm.part_o = (float*)ws;
+  prm.part_lse = (float*)ws + (size_t)splits * Hq * total_q * d;
+  return dispatch<3, T>(prm, d, causal, (hipStream_t)stream);
 }
 
 size_t bwd_ws_bytes(int B, int Nq, int Hq) {
@@ -381,6 +426,56 @@ int fa_fwd_paged_f16(const void* q, const void* k_cache, const void* v_cache, vo
   return run_var<fa::F16>(q, k_cache, v_cache, o, lse, cu_seqlens_q, nullptr, seqused_k, block_table, B,
                           max_seqlen_q, total_q, 0, num_pages, page_size, max_pages, Hq, Hkv, d, causal, scale,
                           stream, true);
+}
+
+size_t fa_fwd_var_splitkv_workspace_bytes(int total_q, int Hq, int d, int num_splits) {
+  return var_splitkv_ws_bytes(total_q, Hq, d, num_splits);
+}
+
+int fa_fwd_var_num_splits(int B, int max_seqlen_q, int key_bound, int Hq, int d) {
+  return var_num_splits(B, max_seqlen_q, key_bound, Hq, d);
+}
+
+int fa_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                          const int* seqused_k, int B, int max_seqlen_q, int total_q, int total_k, int Hq, int Hkv,
+                          int d, int causal, float scale, int num_splits, void* stream) {
+  if (num_splits < 1) return FA_ERR_SHAPE;
+  return run_var<fa::Bf16>(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, seqused_k, nullptr, B, max_seqlen_q,
+                           total_q, total_k, 0, 0, 0, Hq, Hkv, d, causal, scale, stream, false, num_splits, workspace,
+                           workspace_bytes);
+}
+
+int fa_fwd_varlen_splitkv_f16(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                              size_t workspace_bytes, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                              const int* seqused_k, int B, int max_seqlen_q, int total_q, int total_k, int Hq,
+                              int Hkv, int d, int causal, float scale, int num_splits, void* stream) {
+  if (num_splits < 1) return FA_ERR_SHAPE;
+  return run_var<fa::F16>(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, seqused_k, nullptr, B, max_seqlen_q,
+                          total_q, total_k, 0, 0, 0, Hq, Hkv, d, causal, scale, stream, false, num_splits, workspace,
+                          workspace_bytes);
+}
+
+int fa_fwd_paged_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, const int* cu_seqlens_q, const int* seqused_k,
+                         const int* block_table, int B, int max_seqlen_q, int total_q, int num_pages, int page_size,
+                         int max_pages, int Hq, int Hkv, int d, int causal, float scale, int num_splits,
+                         void* stream) {
+  if (num_splits < 1) return FA_ERR_SHAPE;
+  return run_var<fa::Bf16>(q, k_cache, v_cache, o, lse, cu_seqlens_q, nullptr, seqused_k, block_table, B,
+                           max_seqlen_q, total_q, 0, num_pages, page_size, max_pages, Hq, Hkv, d, causal, scale,
+                           stream, true, num_splits, workspace, workspace_bytes);
+}
+
+int fa_fwd_paged_splitkv_f16(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                             void* workspace, size_t workspace_bytes, const int* cu_seqlens_q,
+                             const int* seqused_k, const int* block_table, int B, int max_seqlen_q, int total_q,
+                             int num_pages, int page_size, int max_pages, int Hq, int Hkv, int d, int causal,
+                             float scale, int num_splits, void* stream) {
+  if (num_splits < 1) return FA_ERR_SHAPE;
+  return run_var<fa::F16>(q, k_cache, v_cache, o, lse, cu_seqlens_q, nullptr, seqused_k, block_table, B,
+                          max_seqlen_q, total_q, 0, num_pages, page_size, max_pages, Hq, Hkv, d, causal, scale,
+                          stream, true, num_splits, workspace, workspace_bytes);
 }
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, float q_scale, float k_scale,

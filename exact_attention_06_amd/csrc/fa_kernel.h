@@ -209,11 +209,12 @@ struct Layout {
 };
 
 // VM: 0 dense batch, 1 variable-length batch (packed or paged K/V), 2 dense batch with the
-// key range of each query tile split over several blocks (split-KV).
+// key range of each query tile split over several blocks (split-KV), 3 variable-length batch
+// with split-KV (every sequence's key tiles cut into chunks of tps tiles).
 template <int D, bool CAUSAL, class T, int VM>
 __global__ void __launch_bounds__(TileCfg<D>::NW * 64, TileCfg<D>::WPE)
 fwd_kernel(FwdParams p) {
-  constexpr bool VAR = VM == 1, SPLITK = VM == 2;
+  constexpr bool VAR = VM == 1 || VM == 3, SPLITK = VM == 2 || VM == 3;
   using x8 = typename T::x8;
   using x2 = typename T::x2;
   using L = Layout<D>;
@@ -248,10 +249,10 @@ fwd_kernel(FwdParams p) {
 
   int bh, qt, split = 0;
   if constexpr (SPLITK) {
-    // all blocks of split 0 first, then split 1, ...; within a split the dense order
+    // all blocks of split 0 first, then split 1, ...; within a split the order without splits
     const int per = p.B * p.Hq * p.nqt;
     split = blockIdx.x / per;
-    decode_block<CAUSAL, false>(blockIdx.x - split * per, p, bh, qt);
+    decode_block<CAUSAL || VAR, VAR>(blockIdx.x - split * per, p, bh, qt);
   } else {
     decode_block<CAUSAL || VAR, VAR>(blockIdx.x, p, bh, qt);
   }
@@ -320,9 +321,15 @@ fwd_kernel(FwdParams p) {
   const int wtiles = max(0, min(wtiles_all, t1) - t0);
   const int nfull = max(0, min(nfull_all, t1) - t0);
   const int kfirst = t0 * BC;  // first key of the range
-  if (SPLITK && ntiles == 0) {  // a split past the keys of this query tile: empty partial
+  // row of (split, this head, query q_lane) in the split-KV partials: dense [splits, B*Hq, Nq],
+  // variable-length [splits, Hq, total_q] (packed query rows)
+  auto part_row = [&](int ql) -> size_t {
+    return VAR ? ((size_t)split * p.Hq + hq) * p.total_q + q_row0 + ql
+               : ((size_t)split * p.B * p.Hq + bh) * Nq + ql;
+  };
+  if (SPLITK && (ntiles == 0 || (VAR && kend <= 0))) {  // no key of this split: empty partial
     if (q_lane < Nq) {
-      const size_t row = ((size_t)split * p.B * p.Hq + bh) * Nq + q_lane;
+      const size_t row = part_row(q_lane);
       float* po = p.part_o + row * D;
 #pragma unroll
       for (int md = 0; md < MT2; ++md)
@@ -822,7 +829,7 @@ fwd_kernel(FwdParams p) {
     }
     const float inv = 1.0f / lO;
     if constexpr (SPLITK) {  // normalised fp32 partial and its log-sum-exp
-      const size_t row = ((size_t)split * p.B * p.Hq + bh) * Nq + q_lane;
+      const size_t row = part_row(q_lane);
       float* po = p.part_o + row * D;
 #pragma unroll
       for (int md = 0; md < MT2; ++md)
@@ -889,6 +896,44 @@ __global__ void __launch_bounds__(256) fwd_combine(FwdParams p) {
   const int i = (int)(r - bhq * p.Nq);
   const int b = (int)(bhq / p.Hq), h = (int)(bhq - (size_t)b * p.Hq);
   uint8_t* op = p.o + (((size_t)b * p.Nq + i) * p.Hq + h) * (size_t)(D * 2) + 16 * g;
+  u32x4 w;
+  for (int e = 0; e < 4; ++e)
+    w[e] = __builtin_bit_cast(unsigned, T::cvt2(acc[2 * e] * inv, acc[2 * e + 1] * inv));
+  *(u32x4*)op = w;
+  if (g == 0) p.lse[r] = sum > 0.f ? m + __builtin_amdgcn_logf(sum) * LN2 : -__builtin_inff();
+}
+
+// The same merge for variable-length batches: partials [splits, Hq, total_q, D] and
+// [splits, Hq, total_q]; the result goes to o [total_q, Hq, D] (T) and lse [Hq, total_q].
+// A row whose splits all saw no key keeps O = 0 and LSE = -inf.
+template <int D, class T>
+__global__ void __launch_bounds__(256) fwd_combine_var(FwdParams p) {
+  constexpr int G = D / 8;
+  const size_t rows = (size_t)p.Hq * p.total_q;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * G) return;
+  const size_t r = idx / G;  // h * total_q + i
+  const int g = (int)(idx - r * G);
+  float m = -__builtin_inff();
+  for (int s = 0; s < p.splits; ++s) m = __builtin_fmaxf(m, p.part_lse[s * rows + r]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  if (m != -__builtin_inff()) {
+    for (int s = 0; s < p.splits; ++s) {
+      const float w = __builtin_amdgcn_exp2f((p.part_lse[s * rows + r] - m) * LOG2E);
+      sum += w;
+      const f32x4* po = (const f32x4*)(p.part_o + (s * rows + r) * D + 8 * g);
+      const f32x4 a = po[0], bq = po[1];
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += w * a[e];
+        acc[4 + e] += w * bq[e];
+      }
+    }
+  }
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  const int h = (int)(r / p.total_q);
+  const size_t i = r - (size_t)h * p.total_q;
+  uint8_t* op = p.o + (i * p.Hq + h) * (size_t)(D * 2) + 16 * g;
   u32x4 w;
   for (int e = 0; e < 4; ++e)
     w[e] = __builtin_bit_cast(unsigned, T::cvt2(acc[2 * e] * inv, acc[2 * e + 1] * inv));

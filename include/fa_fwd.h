@@ -183,6 +183,59 @@ int fa_fwd_paged_f16(const void* q, const void* k_cache, const void* v_cache, vo
                      int B, int max_seqlen_q, int total_q, int num_pages, int page_size,
                      int max_pages, int Hq, int Hkv, int d, int causal, float scale, void* stream);
 
+/* Split-KV forms of the two calls above, for batches whose sequences have few query rows and
+ * many keys (decoding): the key tiles of every sequence are cut into chunks of tps tiles,
+ * tps = ceil(ceil(Kmax / key_tile) / num_splits), where Kmax bounds every sequence's key count
+ * (fa_fwd_paged_splitkv: max_pages * page_size; fa_fwd_varlen_splitkv: total_k) and key_tile
+ * is 64 keys (d = 128) or 32 (d = 256). Chunk s of a sequence is computed by its own
+ * workgroups, which write their normalised output O_s and LSE_s (fp32) to the workspace; a
+ * second kernel merges them exactly, LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s
+ * (the merge of the dense split-KV call above). The result is the operation of
+ * fa_fwd_varlen / fa_fwd_paged (same layouts, masks, empty-row convention and errors); only
+ * the rounding order differs. Packed query rows that belong to no sequence receive
+ * unspecified values (the calls without splits leave them untouched).
+ *
+ * workspace: caller-owned device memory of at least
+ *   fa_fwd_var_splitkv_workspace_bytes(total_q, Hq, d, num_splits) = num_splits*Hq*total_q*(d+1)*4
+ * bytes, 16-byte aligned (FA_ERR_WORKSPACE otherwise); contents on entry do not matter.
+ * num_splits: 1..256 (FA_ERR_SHAPE otherwise). */
+size_t fa_fwd_var_splitkv_workspace_bytes(int total_q, int Hq, int d, int num_splits);
+
+/* The library's split count for such a batch (0: call the form without splits). key_bound is
+ * the Kmax above. Measured on MI355X: decode-shaped batches (at most 64 query rows per
+ * sequence) over long caches gain about a third in K/V bandwidth; prefill batches only lose
+ * (the partials' traffic), so they get 0. */
+int fa_fwd_var_num_splits(int B, int max_seqlen_q, int key_bound, int Hq, int d);
+
+int fa_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          const int* cu_seqlens_q, const int* cu_seqlens_k, const int* seqused_k,
+                          int B, int max_seqlen_q, int total_q, int total_k,
+                          int Hq, int Hkv, int d, int causal, float scale, int num_splits, void* stream);
+
+/* Same as fa_fwd_varlen_splitkv with fp16 q/k/v/o. */
+int fa_fwd_varlen_splitkv_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* workspace, size_t workspace_bytes,
+                              const int* cu_seqlens_q, const int* cu_seqlens_k, const int* seqused_k,
+                              int B, int max_seqlen_q, int total_q, int total_k,
+                              int Hq, int Hkv, int d, int causal, float scale, int num_splits,
+                              void* stream);
+
+int fa_fwd_paged_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes,
+                         const int* cu_seqlens_q, const int* seqused_k, const int* block_table,
+                         int B, int max_seqlen_q, int total_q, int num_pages, int page_size,
+                         int max_pages, int Hq, int Hkv, int d, int causal, float scale, int num_splits,
+                         void* stream);
+
+/* Same as fa_fwd_paged_splitkv with fp16 q/k/v/o. */
+int fa_fwd_paged_splitkv_f16(const void* q, const void* k_cache, const void* v_cache, void* o,
+                             float* lse, void* workspace, size_t workspace_bytes,
+                             const int* cu_seqlens_q, const int* seqused_k, const int* block_table,
+                             int B, int max_seqlen_q, int total_q, int num_pages, int page_size,
+                             int max_pages, int Hq, int Hkv, int d, int causal, float scale,
+                             int num_splits, void* stream);
+
 /* Static, NUL-terminated description of an fa_status code (never NULL). */
 const char* fa_strerror(int code);
 

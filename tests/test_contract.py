@@ -36,7 +36,10 @@ def test_library_exports_every_header_symbol():
     assert set(names) == {"fa_fwd", "fa_fwd_f16", "fa_strerror", "fa_fwd_check", "fa_bwd", "fa_bwd_f16",
                           "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_f16", "fa_fwd_paged",
                           "fa_fwd_paged_f16", "fa_fwd_splitkv", "fa_fwd_splitkv_f16",
-                          "fa_fwd_splitkv_workspace_bytes", "fa_fwd_num_splits", "fa_fwd_fp8"}
+                          "fa_fwd_splitkv_workspace_bytes", "fa_fwd_num_splits", "fa_fwd_fp8",
+                          "fa_fwd_var_splitkv_workspace_bytes", "fa_fwd_varlen_splitkv",
+                          "fa_fwd_varlen_splitkv_f16", "fa_fwd_paged_splitkv", "fa_fwd_paged_splitkv_f16",
+                          "fa_fwd_var_num_splits"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -298,3 +301,69 @@ def test_fp8_python_layer_checks_dtype():
     q = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward_fp8(q, q, q)
+
+
+def _var_ws_ok(a):
+    return 4 * a["Hq"] * a["total_q"] * (a["d"] + 1) * 4
+
+
+def _varlen_split(fn, **kw):
+    a = dict(VGOOD, **kw)
+    ws, wsb = a.get("ws", A + 0x900), a.get("wsb", _var_ws_ok(a))
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], ws, wsb, a["cu_q"], a["cu_k"], a["used"], a["B"],
+              a["max_q"], a["total_q"], a["total_k"], a["Hq"], a["Hkv"], a["d"], a["causal"],
+              ctypes.c_float(a["scale"]), a.get("splits", 4), None)
+
+
+def _paged_split(fn, **kw):
+    a = dict(VGOOD, **kw)
+    ws, wsb = a.get("ws", A + 0x900), a.get("wsb", _var_ws_ok(a))
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], ws, wsb, a["cu_q"], a["used"], a["bt"], a["B"],
+              a["max_q"], a["total_q"], a["num_pages"], a["page_size"], a["max_pages"], a["Hq"], a["Hkv"], a["d"],
+              a["causal"], ctypes.c_float(a["scale"]), a.get("splits", 4), None)
+
+
+def test_var_splitkv_workspace_size():
+    lib = _lib.load()
+    assert lib.fa_fwd_var_splitkv_workspace_bytes(300, 8, 128, 3) == 3 * 8 * 300 * 129 * 4
+    assert lib.fa_fwd_var_splitkv_workspace_bytes(300, 8, 256, 1) == 8 * 300 * 257 * 4
+    assert lib.fa_fwd_var_splitkv_workspace_bytes(300, 8, 512, 2) == 0
+    assert lib.fa_fwd_var_splitkv_workspace_bytes(300, 8, 128, 0) == 0
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd_varlen_splitkv", "fa_fwd_varlen_splitkv_f16"])
+def test_varlen_splitkv_rejects_before_any_hip_call(entry):
+    fn = getattr(_lib.load(), entry)
+    for f in ("q", "cu_q", "cu_k"):
+        assert _varlen_split(fn, **{f: 0}) == _lib.FA_ERR_NULL, f
+    assert _varlen_split(fn, Hkv=3) == _lib.FA_ERR_SHAPE
+    assert _varlen_split(fn, d=512) == _lib.FA_ERR_HEADDIM
+    assert _varlen_split(fn, splits=0) == _lib.FA_ERR_SHAPE
+    assert _varlen_split(fn, splits=257) == _lib.FA_ERR_SHAPE
+    assert _varlen_split(fn, ws=0) == _lib.FA_ERR_WORKSPACE
+    assert _varlen_split(fn, ws=A + 4) == _lib.FA_ERR_WORKSPACE
+    a = dict(VGOOD)
+    assert _varlen_split(fn, wsb=_var_ws_ok(a) - 1) == _lib.FA_ERR_WORKSPACE
+    assert _varlen_split(fn, scale=math.nan) == _lib.FA_ERR_SCALE
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd_paged_splitkv", "fa_fwd_paged_splitkv_f16"])
+def test_paged_splitkv_rejects_before_any_hip_call(entry):
+    fn = getattr(_lib.load(), entry)
+    for f in ("q", "used", "bt"):
+        assert _paged_split(fn, **{f: 0}) == _lib.FA_ERR_NULL, f
+    assert _paged_split(fn, page_size=100) == _lib.FA_ERR_PAGE
+    assert _paged_split(fn, d=64) == _lib.FA_ERR_HEADDIM
+    assert _paged_split(fn, splits=0) == _lib.FA_ERR_SHAPE
+    assert _paged_split(fn, ws=0) == _lib.FA_ERR_WORKSPACE
+    assert _paged_split(fn, o=A + 2) == _lib.FA_ERR_ALIGN
+
+
+def test_var_num_splits_choice():
+    assert fa.var_num_splits(128, 16, 32768, 8, 256) == 8        # decode over long caches
+    assert fa.var_num_splits(128, 16, 32768, 8, 128) == 8
+    assert fa.var_num_splits(8, 4096, 32768, 16, 128) == 0       # prefill: never
+    assert fa.var_num_splits(8, 65, 32768, 16, 128) == 0
+    assert fa.var_num_splits(4, 1, 512, 8, 256) == 0             # short caches: 16 tiles
+    assert 2 <= fa.var_num_splits(4, 1, 2048, 8, 256) < 8        # 64 tiles
+    assert fa.var_num_splits(4, 1, 2048, 8, 512) == 0            # unsupported head dim

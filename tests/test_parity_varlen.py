@@ -42,26 +42,26 @@ def _compare(name, o, lse, O_ref, L_ref):
         f"{name}: O max {mx:.3e} mean {mean:.3e} LSE max {lmx:.3e}"
 
 
-def _run_varlen(name, Lq, Lk, Hq, Hkv, d, causal, seed, used=None, dtype=torch.bfloat16):
+def _run_varlen(name, Lq, Lk, Hq, Hkv, d, causal, seed, used=None, dtype=torch.bfloat16, splits=0):
     q, k, v, cu_q, cu_k = W.make_varlen(Lq, Lk, Hq, Hkv, d, seed, dtype)
     scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
     _say(f"[gpu] varlen {name} B={len(Lq)} Lq={list(Lq)[:8]} Lk={list(Lk)[:8]} used={used} Hq={Hq} "
-         f"Hkv={Hkv} d={d} causal={causal} {dtype}")
+         f"Hkv={Hkv} d={d} causal={causal} {dtype} splits={splits}")
     used_t = None if used is None else torch.tensor(used, dtype=torch.int32)
     o, lse = fa.forward_varlen(q.cuda(), k.cuda(), v.cuda(), cu_q.cuda(), cu_k.cuda(), max(Lq), causal=causal,
-                               scale=scale, seqused_k=None if used_t is None else used_t.cuda())
+                               scale=scale, seqused_k=None if used_t is None else used_t.cuda(), num_splits=splits)
     torch.cuda.synchronize()
     O_ref, L_ref = attention_varlen_ref(q, k, v, cu_q, cu_k, causal, scale, seqused_k=used_t)
     _compare(name, o, lse, O_ref, L_ref)
 
 
-def _run_paged(name, Lq, used, page_size, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16):
+def _run_paged(name, Lq, used, page_size, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, splits=0):
     q, kc, vc, cu_q, used_t, bt = W.make_paged(Lq, used, page_size, Hq, Hkv, d, seed, dtype)
     scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
     _say(f"[gpu] paged {name} B={len(Lq)} Lq={list(Lq)[:8]} used={list(used)[:8]} page={page_size} "
-         f"pages={kc.shape[0]} Hq={Hq} Hkv={Hkv} d={d} causal={causal} {dtype}")
+         f"pages={kc.shape[0]} Hq={Hq} Hkv={Hkv} d={d} causal={causal} {dtype} splits={splits}")
     o, lse = fa.forward_paged(q.cuda(), kc.cuda(), vc.cuda(), cu_q.cuda(), used_t.cuda(), bt.cuda(), max(Lq),
-                              causal=causal, scale=scale)
+                              causal=causal, scale=scale, num_splits=splits)
     torch.cuda.synchronize()
     O_ref, L_ref = attention_paged_ref(q, kc, vc, cu_q, used_t, bt, causal, scale)
     _compare(name, o, lse, O_ref, L_ref)
@@ -188,3 +188,62 @@ def test_random_varlen(case):
 def test_random_paged(case):
     name, Lq, used, page, Hq, Hkv, d, causal, seed = case
     _run_paged(name, Lq, used, page, Hq, Hkv, d, causal, seed)
+
+
+
+# ---------------------------------------------------------------- split-KV forms
+
+@pytest.mark.parametrize("splits", [2, 3, 8])
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("case", VARLEN, ids=[c[0] for c in VARLEN])
+def test_varlen_splitkv(case, causal, splits):
+    name, Lq, Lk, Hq, Hkv, d, seed, used = case
+    _run_varlen(f"{name}/s{splits}", Lq, Lk, Hq, Hkv, d, causal, seed, used, splits=splits)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("case", PAGED, ids=[c[0] for c in PAGED])
+def test_paged_splitkv(case, causal, splits):
+    name, Lq, used, page, Hq, Hkv, d, seed = case
+    _run_paged(f"{name}/s{splits}", Lq, used, page, Hq, Hkv, d, causal, seed, splits=splits)
+
+
+@pytest.mark.parametrize("case", RV, ids=[c[0] for c in RV])
+def test_random_varlen_splitkv(case):
+    name, Lq, Lk, Hq, Hkv, d, causal, seed, used = case
+    _run_varlen(name + "/split", Lq, Lk, Hq, Hkv, d, causal, seed, used, splits=1 + seed % 7)
+
+
+@pytest.mark.parametrize("case", RP, ids=[c[0] for c in RP])
+def test_random_paged_splitkv(case):
+    name, Lq, used, page, Hq, Hkv, d, causal, seed = case
+    _run_paged(name + "/split", Lq, used, page, Hq, Hkv, d, causal, seed, splits=1 + seed % 9)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_fp16_splitkv(d):
+    _run_varlen(f"fp16_varlen_split_d{d}", (17, 200), (300, 200), 2, 1, d, True, 65 + d, dtype=torch.float16,
+                splits=3)
+    _run_paged(f"fp16_paged_split_d{d}", (3, 64), (700, 64), 128, 2, 1, d, True, 66 + d, dtype=torch.float16,
+               splits=4)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_one_split_equals_no_split_bitwise(d):
+    # one split: each block covers all keys, the merge has one weight of exactly 1
+    q, kc, vc, cu_q, used, bt = W.make_paged((1, 9, 200), (700, 1000, 300), 128, 4, 2, d, 67)
+    for causal in (False, True):
+        o1, l1 = fa.forward_paged(q.cuda(), kc.cuda(), vc.cuda(), cu_q.cuda(), used.cuda(), bt.cuda(), 200,
+                                  causal=causal)
+        o2, l2 = fa.forward_paged(q.cuda(), kc.cuda(), vc.cuda(), cu_q.cuda(), used.cuda(), bt.cuda(), 200,
+                                  causal=causal, num_splits=1)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), (d, causal)
+
+
+def test_decode_workload_splitkv():
+    w = [x for x in W.var_workloads() if x.paged and "decode" in x.name][0]
+    for splits in (4, 16):
+        _run_paged(f"{w.name}/s{splits}", w.seqlens_q, w.seqlens_k, w.page_size, w.Hq, w.Hkv, w.d, True, w.seed,
+                   splits=splits)
