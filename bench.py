@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--gemm-n", type=int, default=0,
+                    help="only time torch.matmul on two n x n bf16 matrices (the platform GEMM's "
+                         "MFMA throughput on this board, for context)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -193,6 +196,33 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_mib": args.copy_mib, "bytes_read": n, "bytes_written": n,
                           "launches": max(1, args.steps)}), flush=True)
+        return
+
+    if args.gemm_n:
+        # The platform's own dense bf16 GEMM (hipBLASLt behind torch.matmul) under the same
+        # board power limit: a practical ceiling for MFMA-bound kernels, reported beside the
+        # published peak.
+        n = args.gemm_n
+        g = torch.Generator(device="cuda")
+        g.manual_seed(0)
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(max(1, args.warmup)):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.steps)
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"gemm_n": n, "dtype": "bf16", "ms": round(ms, 4), "tflops": round(tf, 1),
+                          "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "launches": reps}), flush=True)
+        del c
         return
 
     w = W.by_name(args.workload)
