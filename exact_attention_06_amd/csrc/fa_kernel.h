@@ -33,6 +33,9 @@
 //     wave sees a tile max above m + TAU; until then p <= 2^TAU;
 //   * two row sums: lO = sum of the rounded P actually fed to the MFMA (normalises O, so the
 //     rounding of P cancels in O = (P_b V) / sum P_b) and lL = fp32 sum of p (feeds the LSE).
+//     lO is taken on the matrix cores: a 16x16x32 MFMA of a 0/1 selector and a P fragment
+//     gives every lane the 16-key sum of its own row (a VALU dot per pair of p cost as
+//     much as three plain VALU ops beside the MFMAs).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -68,12 +71,19 @@ struct Bf16 {
     f32x2 f = {a, b};
     return __builtin_convertvector(f, x2);  // one v_cvt_pk_bf16_f32, round to nearest even
   }
+  static __device__ __forceinline__ f32x4 mfma16(x8 a, x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
   static __device__ __forceinline__ float dot2(x2 a, x2 b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
   }
   static __device__ __forceinline__ x2 ones() {
     x2 r = {(__bf16)1.0f, (__bf16)1.0f};
     return r;
+  }
+  static __device__ __forceinline__ x8 splat(float v) {
+    const __bf16 h = (__bf16)v;
+    return x8{h, h, h, h, h, h, h, h};
   }
 };
 
@@ -87,12 +97,19 @@ struct F16 {
     f32x2 f = {a, b};
     return __builtin_convertvector(f, x2);
   }
+  static __device__ __forceinline__ f32x4 mfma16(x8 a, x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
   static __device__ __forceinline__ float dot2(x2 a, x2 b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
   }
   static __device__ __forceinline__ x2 ones() {
     x2 r = {(_Float16)1.0f, (_Float16)1.0f};
     return r;
+  }
+  static __device__ __forceinline__ x8 splat(float v) {
+    const _Float16 h = (_Float16)v;
+    return x8{h, h, h, h, h, h, h, h};
   }
 };
 
@@ -372,8 +389,20 @@ fwd_kernel(FwdParams p) {
   for (int i = 0; i < MT2; ++i) acc[i] = f32x16{};
   float m_run = -__builtin_inff();
   float lL = 0.f, lO = 0.f;
-  const float c = p.c;
+  // PIPE (hd128) takes lO on the matrix cores; SEQ (hd256) has no registers to spare for the
+  // selector and the accumulator and keeps a VALU dot per pair (per lane half, into lO).
+  constexpr bool MMA_ROWSUM = TileCfg<D>::MODE == PIPE;
   const x2 one2 = T::ones();
+  // lO4 accumulates sel x P fragment (16x16x32 MFMA). B = a P fragment read as 16 columns x
+  // 32 k: lanes 16g..16g+15 hold rows 16(g&1)..+15 of the 32-row block, key half g>>1 of the
+  // 16-key step. A (row i = lane%16, k-slice g = lane/16) is 1 where g&1 == (i>>2)&1, so
+  // output rows 0-3 and 8-11 sum the rows 0-15 of the block and rows 4-7 and 12-15 the rows
+  // 16-31; output lane l holds rows 4(l/16)..+3 of column l%16, which is then the sum over
+  // all 16 keys of row l%32 - the row the lane owns - in each of its four registers.
+  f32x4 lO4 = {};
+  const int sel_lane = threadIdx.x & 63;
+  const x8 sel = T::splat((((sel_lane >> 4) & 1) == ((sel_lane >> 2) & 1)) ? 1.f : 0.f);
+  const float c = p.c;
 
   // ---- K/V tiles: buffer loads straight into LDS (buffer_load ... lds). One instruction
   //      of a wave fills 64 consecutive 16-byte LDS slots (M0 base + 16 * lane); a padded row
@@ -564,7 +593,10 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < MT2; ++i) acc[i] *= alpha;
       lL *= alpha;
-      lO *= alpha;
+      if constexpr (MMA_ROWSUM)
+        lO4 *= alpha;
+      else
+        lO *= alpha;
       m_run = mnew;
     }
   };
@@ -572,7 +604,9 @@ fwd_kernel(FwdParams p) {
   // p = exp2(s*c - m), rounded to the MFMA type; lL += sum p (fp32), lO += sum of rounded p.
   // With pl, also lo = round(p - hi), so hi + lo carries ~16 significant bits.
   auto softmax = [&](const f32x16 (&s)[MT1], x8 (&pf)[KS2], x8* pl) {
-    const float negm = -m_run;
+    // A row that sees no key so far (m = -inf, all scores -inf) gets p = 0, not NaN: the
+    // row-sum MFMA reads two rows through one B column, and 0 * NaN would reach the other.
+    const float negm = m_run == -__builtin_inff() ? 0.f : -m_run;
     float sumL = 0.f, sumO = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT1; ++mt)
@@ -582,19 +616,27 @@ fwd_kernel(FwdParams p) {
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r + 1], c, negm));
         sumL += p0 + p1;
         const x2 pb = T::cvt2(p0, p1);
-        sumO = T::dot2(pb, one2, sumO);
+        if constexpr (!MMA_ROWSUM) sumO = T::dot2(pb, one2, sumO);
         const int u = mt * 2 + (r >> 3);
         pf[u][(r & 7)] = pb[0];
         pf[u][(r & 7) + 1] = pb[1];
         if (pl) {
           const x2 lo = T::cvt2(p0 - (float)pb[0], p1 - (float)pb[1]);
-          sumO = T::dot2(lo, one2, sumO);
+          if constexpr (!MMA_ROWSUM) sumO = T::dot2(lo, one2, sumO);
           pl[u][(r & 7)] = lo[0];
           pl[u][(r & 7) + 1] = lo[1];
         }
       }
     lL += sumL;
-    lO += sumO;
+    if constexpr (MMA_ROWSUM) {
+#pragma unroll
+      for (int u = 0; u < KS2; ++u) {
+        lO4 = T::mfma16(sel, pf[u], lO4);
+        if (pl) lO4 = T::mfma16(sel, pl[u], lO4);
+      }
+    } else {
+      lO += sumO;
+    }
   };
 
   if constexpr (TileCfg<D>::MODE == SEQ) {
@@ -691,10 +733,12 @@ fwd_kernel(FwdParams p) {
 
   // Main iteration (unmasked tile j, tile j+1 exists), with an explicit instruction order:
   //   phase 1: each GEMM1(j+1) MFMA is issued with the LDS read PF steps ahead and with one
-  //            slice of the softmax VALU work of tile j (fma, exp, sums, pack of a pair);
+  //            slice of the softmax VALU work of tile j (fma, exp and pack of a pair);
   //            the last steps start reading the V fragments of GEMM2;
-  //   phase 2: each GEMM2(j) MFMA with the V read PF steps ahead and with one slice of the
-  //            row max of tile j+1 (which the next iteration's rescale decision needs).
+  //   phase 2: each GEMM2(j) MFMA with the V read PF steps ahead, one slice of the fp32 row
+  //            sum of tile j and of the row max of tile j+1 (which the next iteration's
+  //            rescale decision needs); after the last MFMA of each 16-key step, the row-sum
+  //            MFMA of that step's rounded P.
   // sched_barrier fences keep each step's instructions together.
   constexpr int PF = D == 256 ? 2 : 4;  // LDS fragment reads issued this many MFMAs ahead
   constexpr int N1 = MT1 * KS1, N2 = MT2 * KS2;
@@ -723,7 +767,7 @@ fwd_kernel(FwdParams p) {
       return __builtin_bit_cast(x8, raw);
     };
     x8 kf[N1], vf[N2], pf[KS2];
-    float sumL0 = 0.f, sumL1 = 0.f, sumO = 0.f;
+    float sumL0 = 0.f, sumL1 = 0.f;
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
     __builtin_amdgcn_sched_barrier(0);
@@ -766,20 +810,12 @@ fwd_kernel(FwdParams p) {
           sumL0 += sc[e / 16][e % 16];
         mx = __builtin_fmaxf(mx, sn[e / 16][e % 16]);
       }
-      if ((i * NPAIR) % N2 == 0) {  // sum of the rounded pair that normalises O
-        const int pi = i * NPAIR / N2, mt = pi / 8, r = (pi % 8) * 2;
-        const int u2 = mt * 2 + (r >> 3);
-        x2 pb;
-        pb[0] = pf[u2][(r & 7)];
-        pb[1] = pf[u2][(r & 7) + 1];
-        sumO = T::dot2(pb, one2, sumO);
-      }
+      if (md == MT2 - 1) lO4 = T::mfma16(sel, pf[u], lO4);  // sum of the rounded P of step u
       // keep this slice in this step (otherwise the reductions are sunk past the interleave)
-      asm volatile("" : "+v"(mx), "+v"(sumL0), "+v"(sumL1), "+v"(sumO));
+      asm volatile("" : "+v"(mx), "+v"(sumL0), "+v"(sumL1));
       __builtin_amdgcn_sched_barrier(0);
     }
     lL += sumL0 + sumL1;
-    lO += sumO;
     mx = __builtin_fmaxf(mx, other_half(mx));
     mt_cur = mx * c;
     __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
@@ -817,7 +853,10 @@ fwd_kernel(FwdParams p) {
 
   // ---- epilogue: combine the two lane halves' sums, normalise, store O and LSE
   lL += other_half(lL);
-  lO += other_half(lO);
+  if constexpr (MMA_ROWSUM)
+    lO = lO4[0];  // already the sum over both lane halves
+  else
+    lO += other_half(lO);
   if (q_lane < Nq) {
     // causal: a row that sees no key of this block's range (VAR: q_lane + cshift < 0; split-KV:
     // a range that starts past the row's last key) stores O = 0, LSE = -inf
