@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA peak (published)
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E (published)
 DEFAULT_WORKLOAD = "hd256_N8192"
 PAGES_B200 = {  # pages' own forward TFLOPS for the hd256 snapshot workloads (B200, context only)
     ("hd256_N1024", False): 950, ("hd256_N2048", False): 1280, ("hd256_N4096", False): 1477,
@@ -164,6 +165,9 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--only-variants", action="store_true",
+                    help="besides the headline workload, run only the serving variants (packed and "
+                         "paged prefill, paged decode); used to profile them")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--gemm-n", type=int, default=0,
@@ -240,8 +244,9 @@ def main():
     log(f"[bench] {w.name} causal={causal}: {ms:.3f} ms/step, {tflops:.1f} TFLOPS "
         f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS:.0f})")
 
+    rest = not args.no_sweep and not args.only_variants  # sweep, short-sequence and fp8 sections
     sweep = []
-    if not args.no_sweep:
+    if rest:
         pts = [x for x in W.hd128_sweep() + W.hd256_sweep() + [W.video()] + W.hd512_sweep()]
         for x in pts:
             qx, kx, vx = gpu_inputs(x, torch)
@@ -263,7 +268,7 @@ def main():
     # backward pass (gradients of sum(O * dO)); FLOPs counted as 2.5x the forward's
     # (five N x N x d products), the usual convention
     backward = []
-    if not args.no_backward:
+    if not args.no_backward and not args.only_variants:
         for name in ("hd128_N8192_mha", "hd256_N8192"):
             x = W.by_name(name)
             qx, kx, vx = gpu_inputs(x, torch)
@@ -293,7 +298,7 @@ def main():
 
     # short sequences, few heads: the plain grid vs split-KV (the library's split count)
     short = []
-    if not args.no_sweep:
+    if rest:
         for (B_, N_, H_, d_) in ((1, 1024, 8, 256), (2, 1024, 8, 256), (1, 2048, 8, 256), (1, 1024, 16, 128)):
             g = torch.Generator(device="cuda")
             g.manual_seed(71)
@@ -329,7 +334,7 @@ def main():
     # fp8 (e4m3) inputs, one dequantisation factor per tensor, bf16 output; priced against the
     # fp8 MFMA peak
     fp8 = []
-    if not args.no_sweep:
+    if rest:
         for name in ("hd128_N8192_mha", "hd256_N8192"):
             x = W.by_name(name)
             qx, kx, vx = gpu_inputs(x, torch)
@@ -361,7 +366,7 @@ def main():
     # serving variants: packed variable-length prefill, paged prefill, paged decode; each without
     # splits and, where the library picks a split count for its shape, split over the keys too
     variants = []
-    if not args.no_sweep:
+    if not args.no_sweep or args.only_variants:
         for x in W.bench_var_workloads():
             mq = max(x.seqlens_q)
             if x.paged:
@@ -394,7 +399,8 @@ def main():
                     ent = {"workload": x.name, "causal": c, "B": x.B, "total_q": sum(x.seqlens_q),
                            "total_k": sum(x.seqlens_k), "Hq": x.Hq, "Hkv": x.Hkv, "d": x.d, "paged": x.paged,
                            "num_splits": ns, "ms": round(m, 4), "tflops": round(t, 1),
-                           "kv_gbps": round(kv_bytes / (m * 1e-3) / 1e9, 1)}
+                           "kv_gbps": round(kv_bytes / (m * 1e-3) / 1e9, 1),
+                           "kv_frac_hbm_peak": round(kv_bytes / (m * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
                     variants.append(ent)
                     log(f"[var] {x.name:26s} {'causal' if c else 'noncausal':9s} splits {ns:2d} {m:8.3f} ms "
                         f"{t:7.1f} TFLOPS K/V {ent['kv_gbps']:7.1f} GB/s")

@@ -188,6 +188,55 @@ __device__ __forceinline__ void decode_block(int bid, const FwdParams& p, int& b
   }
 }
 
+// Non-causal variable-length / paged batches of at most 64 sequences: every block of sequence
+// b costs about its key tiles, the same for all its query tiles, so the order above (highest
+// query tile first) leaves the query tiles 0.. of the longest sequences for the last round.
+// Here the blocks go longest sequence first instead (longest-processing-time order over the
+// CUs): lane l of every wave reads sequence l's lengths, ranks the sequences by key count
+// (ties by index), and the block's entry e = bid / Hq is found in the ranked prefix sums of the
+// query-tile counts. The Hq heads of an entry are consecutive block ids, so head h of all query
+// tiles of a sequence lands on one XCD (bid % 8) close together in time and shares its L2 for
+// that head's K/V; with Hq a multiple of 8 the heads on one XCD are a contiguous (GQA) range.
+// Returns false when the block has no entry (the grid is sized for max_seqlen_q).
+template <int BR, int BC>
+__device__ __forceinline__ bool decode_block_lpt(int bid, const FwdParams& p, int& bh, int& qt) {
+  const int l = threadIdx.x & 63;
+  int nt = 0, key = -1;
+  if (l < p.B) {
+    const int q0 = min(max(p.cu_q[l], 0), p.total_q);
+    const int q1 = min(max(p.cu_q[l + 1], q0), p.total_q);
+    int nk;
+    if (p.block_table == nullptr) {
+      const int k0 = min(max(p.cu_k[l], 0), p.total_k);
+      nk = min(max(p.cu_k[l + 1], k0), p.total_k) - k0;
+    } else {
+      nk = p.max_pages * p.page_size;
+    }
+    if (p.seqused != nullptr) nk = min(nk, max(p.seqused[l], 0));
+    nt = (q1 - q0 + BR - 1) / BR;
+    key = (nk + BC - 1) / BC;
+  }
+  int rank = 0;
+  for (int i = 0; i < p.B; ++i) {
+    const int ki = __builtin_amdgcn_readlane(key, i);
+    rank += (ki > key || (ki == key && i < l)) ? 1 : 0;
+  }
+  int start = 0;
+  for (int i = 0; i < p.B; ++i) {
+    const int ri = __builtin_amdgcn_readlane(rank, i);
+    const int ti = __builtin_amdgcn_readlane(nt, i);
+    start += ri < rank ? ti : 0;
+  }
+  const int e = bid / p.Hq, hslot = bid - e * p.Hq;
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(l < p.B && e >= start && e < start + nt);
+  if (hit == 0) return false;
+  const int b = __builtin_ctzll(hit);
+  qt = e - __builtin_amdgcn_readlane(start, b);
+  const int h = (p.Hq & 7) == 0 ? (hslot & 7) * (p.Hq >> 3) + (hslot >> 3) : hslot;
+  bh = b * p.Hq + h;
+  return true;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
   // raw buffer (stride 0): a load whose offset lies past `bytes` returns zeros
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
@@ -270,6 +319,12 @@ fwd_kernel(FwdParams p) {
     const int per = p.B * p.Hq * p.nqt;
     split = blockIdx.x / per;
     decode_block<CAUSAL || VAR, VAR>(blockIdx.x - split * per, p, bh, qt);
+  } else if constexpr (VAR && !CAUSAL) {
+    if (p.B <= 64) {
+      if (!decode_block_lpt<L::BR, L::BC>(blockIdx.x, p, bh, qt)) return;
+    } else {
+      decode_block<true, true>(blockIdx.x, p, bh, qt);
+    }
   } else {
     decode_block<CAUSAL || VAR, VAR>(blockIdx.x, p, bh, qt);
   }
@@ -472,7 +527,9 @@ fwd_kernel(FwdParams p) {
   // SEQ: LDS fragments are read SPF MFMAs ahead in a fixed order (sched_barrier), so that the
   // read latency hides under the MFMAs before them; left to itself the compiler read them one
   // or two MFMAs ahead.
-  constexpr int SPF1 = 4, SPF2 = 4;
+  // (variable-length causal: 3 ahead; at 4 that kernel spilled and reloaded inside the loop,
+  // -8 to -12%; the dense causal kernel is faster at 4)
+  constexpr int SPF1 = VAR && CAUSAL ? 3 : 4, SPF2 = VAR && CAUSAL ? 3 : 4;
   auto gemm1 = [&](int buf, f32x16 (&s)[MT1]) {
     const uint8_t* kl = (buf ? k_lds1 : k_lds0) + k_rd;
     if constexpr (TileCfg<D>::MODE == SEQ) {
@@ -604,9 +661,11 @@ fwd_kernel(FwdParams p) {
   // p = exp2(s*c - m), rounded to the MFMA type; lL += sum p (fp32), lO += sum of rounded p.
   // With pl, also lo = round(p - hi), so hi + lo carries ~16 significant bits.
   auto softmax = [&](const f32x16 (&s)[MT1], x8 (&pf)[KS2], x8* pl) {
-    // A row that sees no key so far (m = -inf, all scores -inf) gets p = 0, not NaN: the
-    // row-sum MFMA reads two rows through one B column, and 0 * NaN would reach the other.
-    const float negm = m_run == -__builtin_inff() ? 0.f : -m_run;
+    // With the row-sum MFMA, a row that sees no key so far (m = -inf, all scores -inf) gets
+    // p = 0, not NaN: that MFMA reads two rows through one B column, and 0 * NaN would reach
+    // the other. (The per-lane dots keep such a NaN in its own row, which is then stored as
+    // empty: O = 0, LSE = -inf.)
+    const float negm = MMA_ROWSUM && m_run == -__builtin_inff() ? 0.f : -m_run;
     float sumL = 0.f, sumO = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT1; ++mt)
