@@ -247,3 +247,29 @@ def test_decode_workload_splitkv():
     for splits in (4, 16):
         _run_paged(f"{w.name}/s{splits}", w.seqlens_q, w.seqlens_k, w.page_size, w.Hq, w.Hkv, w.d, True, w.seed,
                    splits=splits)
+
+
+# Non-causal batches of at most 64 sequences are dispatched longest sequence first (each block
+# ranks the sequences by key count across a wave); more than 64 take the other order. Cover the
+# limit, one past it, tied key counts, empty sequences and a head count that is not a multiple
+# of 8 (the head order inside an entry differs then).
+def _lpt_lengths(n, seed):
+    g = np.random.default_rng(seed)
+    Lq = [int(x) for x in g.integers(0, 300, n)]
+    Lk = [int(x) for x in g.choice([0, 64, 64, 130, 257, 700], n)]  # many ties, some empty
+    return tuple(Lq), tuple(Lk)
+
+
+@pytest.mark.parametrize("n,Hq,Hkv,d", [(64, 8, 2, 128), (65, 8, 2, 128), (64, 6, 3, 256), (40, 16, 4, 128),
+                                        (1, 8, 8, 256)])
+def test_varlen_longest_first_order(n, Hq, Hkv, d):
+    Lq, Lk = _lpt_lengths(n, 500 + n + d)
+    _run_varlen(f"lpt{n}_h{Hq}_d{d}", Lq, Lk, Hq, Hkv, d, False, 600 + n)
+
+
+@pytest.mark.parametrize("n", [64, 65])
+def test_paged_longest_first_order(n):
+    g = np.random.default_rng(700 + n)
+    Lq = tuple(int(x) for x in g.integers(1, 200, n))
+    used = tuple(int(x) for x in g.choice([0, 128, 128, 300, 640], n))
+    _run_paged(f"lpt_paged{n}", Lq, used, 128, 8, 8, 256, False, 800 + n)
