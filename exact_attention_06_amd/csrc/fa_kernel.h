@@ -188,17 +188,18 @@ __device__ __forceinline__ void decode_block(int bid, const FwdParams& p, int& b
   }
 }
 
-// Non-causal variable-length / paged batches of at most 64 sequences: every block of sequence
-// b costs about its key tiles, the same for all its query tiles, so the order above (highest
-// query tile first) leaves the query tiles 0.. of the longest sequences for the last round.
-// Here the blocks go longest sequence first instead (longest-processing-time order over the
-// CUs): lane l of every wave reads sequence l's lengths, ranks the sequences by key count
+// Variable-length / paged batches of at most 64 sequences go sequence by sequence, longest
+// first: lane l of every wave reads sequence l's lengths, ranks the sequences by key count
 // (ties by index), and the block's entry e = bid / Hq is found in the ranked prefix sums of the
 // query-tile counts. The Hq heads of an entry are consecutive block ids, so head h of all query
 // tiles of a sequence lands on one XCD (bid % 8) close together in time and shares its L2 for
 // that head's K/V; with Hq a multiple of 8 the heads on one XCD are a contiguous (GQA) range.
+// Non-causal, every query tile of a sequence costs the same, and this is the
+// longest-processing-time order over the CUs (the order above, highest query tile first, left
+// the query tiles 0.. of the longest sequences for the last round). Causal, a sequence's query
+// tiles go highest first (the longest blocks of the sequence first).
 // Returns false when the block has no entry (the grid is sized for max_seqlen_q).
-template <int BR, int BC>
+template <int BR, int BC, bool CAUSAL>
 __device__ __forceinline__ bool decode_block_lpt(int bid, const FwdParams& p, int& bh, int& qt) {
   const int l = threadIdx.x & 63;
   int nt = 0, key = -1;
@@ -232,6 +233,7 @@ __device__ __forceinline__ bool decode_block_lpt(int bid, const FwdParams& p, in
   if (hit == 0) return false;
   const int b = __builtin_ctzll(hit);
   qt = e - __builtin_amdgcn_readlane(start, b);
+  if (CAUSAL) qt = __builtin_amdgcn_readlane(nt, b) - 1 - qt;
   const int h = (p.Hq & 7) == 0 ? (hslot & 7) * (p.Hq >> 3) + (hslot >> 3) : hslot;
   bh = b * p.Hq + h;
   return true;
@@ -319,9 +321,9 @@ fwd_kernel(FwdParams p) {
     const int per = p.B * p.Hq * p.nqt;
     split = blockIdx.x / per;
     decode_block<CAUSAL || VAR, VAR>(blockIdx.x - split * per, p, bh, qt);
-  } else if constexpr (VAR && !CAUSAL) {
+  } else if constexpr (VAR) {
     if (p.B <= 64) {
-      if (!decode_block_lpt<L::BR, L::BC>(blockIdx.x, p, bh, qt)) return;
+      if (!decode_block_lpt<L::BR, L::BC, CAUSAL>(blockIdx.x, p, bh, qt)) return;
     } else {
       decode_block<true, true>(blockIdx.x, p, bh, qt);
     }

@@ -3,7 +3,9 @@ fa_fwd_paged and their fp16 forms, through the Python binding) against the fp64 
 in oracle/varlen.py, element by element on every row of every sequence.
 
 Tolerance: the dense path's, O max-abs <= 1e-2 and mean-abs <= 1e-3, LSE max-abs <= 1e-3;
-rows that see no key must come back as exactly O = 0 and LSE = -inf. Causal masks are
+elements with |O_ref| >= 4, where half a bf16 ulp (1.56e-2) already exceeds 1e-2, are held to
+half an ulp plus the same margin as in test_parity.py (rows that see one or two keys reach the
+extremes of V); rows that see no key must come back as exactly O = 0 and LSE = -inf. Causal masks are
 aligned bottom-right (query i of a sequence sees keys j <= i + Lk - Lq).
 """
 
@@ -18,6 +20,7 @@ from oracle import attention_paged_ref, attention_varlen_ref
 pytestmark = pytest.mark.gpu
 
 O_MAX, O_MEAN, LSE_MAX = 1e-2, 1e-3, 1e-3
+EXCESS = O_MAX - 2.0 ** -7
 
 
 def _say(msg):
@@ -25,6 +28,7 @@ def _say(msg):
 
 
 def _compare(name, o, lse, O_ref, L_ref):
+    mant = 7 if o.dtype == torch.bfloat16 else 10
     o = o.float().cpu().numpy().astype(np.float64)
     lse = lse.cpu().numpy().astype(np.float64)
     empty_ref = np.isneginf(L_ref)
@@ -33,13 +37,19 @@ def _compare(name, o, lse, O_ref, L_ref):
     eo = np.abs(o - O_ref)
     el = np.abs(lse[~empty_ref] - L_ref[~empty_ref]) if (~empty_ref).any() else np.zeros(1)
     mx, mean, lmx = float(eo.max()), float(eo.mean()), float(el.max())
+    big = np.abs(O_ref) >= 4.0
+    half_ulp = 0.5 * np.exp2(np.floor(np.log2(np.maximum(np.abs(O_ref), 2.0 ** -126))) - mant)
+    mx_small = float(eo[~big].max()) if (~big).any() else 0.0
+    ex_big = float((eo - half_ulp)[big].max()) if big.any() else 0.0
     n_empty = int(empty_ref.sum())
-    _say(f"  {name}: O max {mx:.3e} mean {mean:.3e} | LSE max {lmx:.3e} | empty rows (x heads) {n_empty}")
+    at = np.unravel_index(int(np.argmax(eo)), eo.shape)
+    _say(f"  {name}: O max {mx:.3e} (|O_ref| there {abs(O_ref[at]):.3f}) mean {mean:.3e} | LSE max {lmx:.3e} | "
+         f"|O_ref|>=4: {int(big.sum())} elems, excess {ex_big:.3e} | empty rows (x heads) {n_empty}")
     if n_empty:
         rows_empty = empty_ref.any(axis=0)
         assert np.all(o[rows_empty] == 0.0), f"{name}: empty rows must be exactly 0"
-    assert mx <= O_MAX and mean <= O_MEAN and lmx <= LSE_MAX, \
-        f"{name}: O max {mx:.3e} mean {mean:.3e} LSE max {lmx:.3e}"
+    assert mx_small <= O_MAX and ex_big <= EXCESS and mean <= O_MEAN and lmx <= LSE_MAX, \
+        f"{name}: O max {mx:.3e} (|O|<4 {mx_small:.3e}, excess {ex_big:.3e}) mean {mean:.3e} LSE max {lmx:.3e}"
 
 
 def _run_varlen(name, Lq, Lk, Hq, Hkv, d, causal, seed, used=None, dtype=torch.bfloat16, splits=0):
@@ -249,10 +259,11 @@ def test_decode_workload_splitkv():
                    splits=splits)
 
 
-# Non-causal batches of at most 64 sequences are dispatched longest sequence first (each block
-# ranks the sequences by key count across a wave); more than 64 take the other order. Cover the
-# limit, one past it, tied key counts, empty sequences and a head count that is not a multiple
-# of 8 (the head order inside an entry differs then).
+# Batches of at most 64 sequences are dispatched sequence by sequence, longest first (each block
+# ranks the sequences by key count across a wave; causal: a sequence's highest query tile
+# first); more than 64 take the other order. Cover the limit, one past it, tied key counts,
+# empty sequences, rows that see no key (causal, more queries than keys) and a head count that
+# is not a multiple of 8 (the head order inside an entry differs then).
 def _lpt_lengths(n, seed):
     g = np.random.default_rng(seed)
     Lq = [int(x) for x in g.integers(0, 300, n)]
@@ -260,16 +271,18 @@ def _lpt_lengths(n, seed):
     return tuple(Lq), tuple(Lk)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
 @pytest.mark.parametrize("n,Hq,Hkv,d", [(64, 8, 2, 128), (65, 8, 2, 128), (64, 6, 3, 256), (40, 16, 4, 128),
                                         (1, 8, 8, 256)])
-def test_varlen_longest_first_order(n, Hq, Hkv, d):
+def test_varlen_longest_first_order(n, Hq, Hkv, d, causal):
     Lq, Lk = _lpt_lengths(n, 500 + n + d)
-    _run_varlen(f"lpt{n}_h{Hq}_d{d}", Lq, Lk, Hq, Hkv, d, False, 600 + n)
+    _run_varlen(f"lpt{n}_h{Hq}_d{d}", Lq, Lk, Hq, Hkv, d, causal, 600 + n)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
 @pytest.mark.parametrize("n", [64, 65])
-def test_paged_longest_first_order(n):
+def test_paged_longest_first_order(n, causal):
     g = np.random.default_rng(700 + n)
     Lq = tuple(int(x) for x in g.integers(1, 200, n))
     used = tuple(int(x) for x in g.choice([0, 128, 128, 300, 640], n))
-    _run_paged(f"lpt_paged{n}", Lq, used, 128, 8, 8, 256, False, 800 + n)
+    _run_paged(f"lpt_paged{n}", Lq, used, 128, 8, 8, 256, causal, 800 + n)
