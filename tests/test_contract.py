@@ -254,6 +254,11 @@ def test_num_splits_choice():
     assert fa.num_splits(1, 1024, 1024, 8, 256, causal=True) > 1
     assert fa.num_splits(1, 100, 100, 8, 256) == 1  # too few key tiles to split
     assert fa.num_splits(4, 1024, 1024, 8, 256) == 1
+    assert fa.num_splits(2, 1024, 1024, 8, 256) == 1                # 128 workgroups, 1k keys
+    assert fa.num_splits(2, 1024, 1024, 8, 256, causal=True) == 2
+    assert fa.num_splits(1, 2048, 2048, 8, 256) == 2                # 128 workgroups, 2k keys
+    assert fa.num_splits(1, 4096, 4096, 8, 256) == 1
+    assert fa.num_splits(1, 4096, 4096, 8, 256, causal=True) == 3
     for shape in [(1, 1024, 1024, 8, 256), (1, 1024, 1024, 16, 128), (2, 2048, 2048, 8, 256)]:
         s = fa.num_splits(*shape)
         assert 1 <= s <= 4
