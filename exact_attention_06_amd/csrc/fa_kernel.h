@@ -918,32 +918,28 @@ fwd_kernel(FwdParams p) {
     lO = lO4[0];  // already the sum over both lane halves
   else
     lO += other_half(lO);
-  if (q_lane < Nq) {
-    // causal: a row that sees no key of this block's range (VAR: q_lane + cshift < 0; split-KV:
-    // a range that starts past the row's last key) stores O = 0, LSE = -inf
-    const bool empty = (VAR || SPLITK) && CAUSAL && q_lane + cshift < kfirst;
-    if (empty) {
-      lO = 1.f;
+  // causal: a row that sees no key of this block's range (VAR: q_lane + cshift < 0; split-KV:
+  // a range that starts past the row's last key) stores O = 0, LSE = -inf
+  const bool empty = (VAR || SPLITK) && CAUSAL && q_lane + cshift < kfirst;
+  if (empty) {
+    lO = 1.f;
 #pragma unroll
-      for (int md = 0; md < MT2; ++md) acc[md] = f32x16{};
-    }
+    for (int md = 0; md < MT2; ++md) acc[md] = f32x16{};
+  }
+  if constexpr (!SPLITK) {
+    // O leaves through LDS: a lane holds 8-byte pieces of one row (lanes 0-31 = 32 rows, so a
+    // direct store writes 32 rows 4 KB apart per instruction, and the workgroup's slot stays
+    // busy until those scattered stores drain). The wave writes its 32 x D tile into its own
+    // part of the K/V buffers (free: every wave is past the last tile's barrier) and reads it
+    // back as whole rows, 16 bytes per lane, so each store instruction covers complete rows.
+    constexpr int RS = D * 2 + 16;  // LDS row pitch of the staged tile (bytes)
+    constexpr int WB = 32 * RS;     // bytes per wave
+    constexpr int OBJ = L::KBUF < L::VBUF ? L::KBUF : L::VBUF;
+    constexpr int WPO = OBJ / WB;   // waves per K/V buffer
+    static_assert(WPO >= 1 && (NW + WPO - 1) / WPO <= 4, "the staged O tiles fit in the K/V buffers");
+    const int wo = wave / WPO;
+    uint8_t* const ost = (wo == 0 ? lds0_v : wo == 1 ? lds1_v : wo == 2 ? lds2_k : lds3_k) + (wave % WPO) * WB;
     const float inv = 1.0f / lO;
-    if constexpr (SPLITK) {  // normalised fp32 partial and its log-sum-exp
-      const size_t row = part_row(q_lane);
-      float* po = p.part_o + row * D;
-#pragma unroll
-      for (int md = 0; md < MT2; ++md)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 w;
-          for (int e = 0; e < 4; ++e) w[e] = acc[md][4 * i + e] * inv;
-          *(f32x4*)(po + 32 * md + 8 * i + 4 * hh) = w;
-        }
-      if (hh == 0)
-        p.part_lse[row] = empty ? -__builtin_inff() : (m_run + __builtin_amdgcn_logf(lL)) * LN2;
-      return;
-    }
-    uint8_t* op = p.o + ((q_row0 + q_lane) * p.Hq + hq) * (size_t)(D * 2);
 #pragma unroll
     for (int md = 0; md < MT2; ++md)
 #pragma unroll
@@ -953,11 +949,34 @@ fwd_kernel(FwdParams p) {
         u32x2 w;
         w[0] = __builtin_bit_cast(unsigned, a);
         w[1] = __builtin_bit_cast(unsigned, bb);
-        const int d = 32 * md + 8 * i + 4 * hh;
-        *(u32x2*)(op + d * 2) = w;
+        *(u32x2*)(ost + l32 * RS + (32 * md + 8 * i + 4 * hh) * 2) = w;
       }
-    if (hh == 0)
+    constexpr int CPL = D * 2 / 16, RPI = 64 / CPL;  // 16-byte chunks per row, rows per read
+    const size_t o_row = (size_t)p.Hq * (D * 2);
+    uint8_t* const o0 = p.o + ((q_row0 + qw0) * p.Hq + hq) * (size_t)(D * 2);
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int r = it * RPI + lane / CPL, ch = lane % CPL;
+      const u32x4 v = *(const u32x4*)(ost + r * RS + ch * 16);
+      if (qw0 + r < Nq) *(u32x4*)(o0 + r * o_row + ch * 16) = v;
+    }
+    if (q_lane < Nq && hh == 0)
       p.lse[lse0 + q_lane] = empty ? -__builtin_inff() : (m_run + __builtin_amdgcn_logf(lL)) * LN2;
+    return;
+  }
+  if (q_lane < Nq) {  // split-KV: the normalised fp32 partial and its log-sum-exp
+    const float inv = 1.0f / lO;
+    const size_t row = part_row(q_lane);
+    float* po = p.part_o + row * D;
+#pragma unroll
+    for (int md = 0; md < MT2; ++md)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 w;
+        for (int e = 0; e < 4; ++e) w[e] = acc[md][4 * i + e] * inv;
+        *(f32x4*)(po + 32 * md + 8 * i + 4 * hh) = w;
+      }
+    if (hh == 0) p.part_lse[row] = empty ? -__builtin_inff() : (m_run + __builtin_amdgcn_logf(lL)) * LN2;
   }
 }
 
