@@ -311,22 +311,37 @@ fwd_fp8_kernel(FwdParams p) {
   // ---- epilogue: O = v_scale * O_acc / sum(rounded P); LSE from the fp32 sum of p
   lL += other_half(lL);
   const float lO = acc[MT2][0];
-  if (q_lane < Nq) {
-    const float inv = p.v_scale / lO;
-    uint8_t* op = p.o + (((size_t)b * Nq + q_lane) * p.Hq + hq) * (size_t)(D * 2);
+  // O leaves through LDS as whole rows (see the bf16 kernel's epilogue): wave w writes its
+  // 32 x D bf16 tile into the w-th K/V buffer (a buffer is exactly 32 rows of 2D bytes; every
+  // wave is past the last tile's barrier), 16-byte chunk k of row r at chunk k ^ (r mod the
+  // chunks per row) so that the 32 rows of a write and the chunks of a read spread over the
+  // banks, and reads it back 16 bytes per lane for full-row stores.
+  static_assert(32 * D * 2 == C::TB, "a wave's O tile fills one K/V buffer");
+  constexpr int CPL = D * 2 / 16, RPI = 64 / CPL;  // 16-byte chunks per row, rows per read
+  uint8_t* const ost = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+  const float inv = p.v_scale / lO;
 #pragma unroll
-    for (int md = 0; md < MT2; ++md)
+  for (int md = 0; md < MT2; ++md)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x2 a = Bf16::cvt2(acc[md][4 * i + 0] * inv, acc[md][4 * i + 1] * inv);
-        const bf16x2 bb = Bf16::cvt2(acc[md][4 * i + 2] * inv, acc[md][4 * i + 3] * inv);
-        u32x2 w;
-        w[0] = __builtin_bit_cast(unsigned, a);
-        w[1] = __builtin_bit_cast(unsigned, bb);
-        *(u32x2*)(op + (32 * md + 8 * i + 4 * hh) * 2) = w;
-      }
-    if (hh == 0) p.lse[((size_t)b * p.Hq + hq) * Nq + q_lane] = (m_run + __builtin_amdgcn_logf(lL)) * LN2;
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 a = Bf16::cvt2(acc[md][4 * i + 0] * inv, acc[md][4 * i + 1] * inv);
+      const bf16x2 bb = Bf16::cvt2(acc[md][4 * i + 2] * inv, acc[md][4 * i + 3] * inv);
+      u32x2 w;
+      w[0] = __builtin_bit_cast(unsigned, a);
+      w[1] = __builtin_bit_cast(unsigned, bb);
+      const int k = 4 * md + i;  // chunk of columns 32md + 8i .. +7; this lane's half at 8hh
+      *(u32x2*)(ost + l32 * (D * 2) + ((k ^ (l32 & (CPL - 1))) * 16) + 8 * hh) = w;
+    }
+  const size_t o_row = (size_t)p.Hq * (D * 2);
+  uint8_t* const o0 = p.o + (((size_t)b * Nq + qw0) * p.Hq + hq) * (size_t)(D * 2);
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int r = it * RPI + lane / CPL, ch = lane % CPL;
+    const u32x4 v = *(const u32x4*)(ost + r * (D * 2) + ((ch ^ (r & (CPL - 1))) * 16));
+    if (qw0 + r < Nq) *(u32x4*)(o0 + r * o_row + ch * 16) = v;
   }
+  if (q_lane < Nq && hh == 0)
+    p.lse[((size_t)b * p.Hq + hq) * Nq + q_lane] = (m_run + __builtin_amdgcn_logf(lL)) * LN2;
 }
 
 }  // namespace fa

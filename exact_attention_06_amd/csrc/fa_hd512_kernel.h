@@ -279,12 +279,36 @@ fwd_hd512_kernel(FwdParams p) {
   }
   for (; j < ntiles; ++j) iteration(j, j & 1, F{}, U{});
 
-  // ---- epilogue: this wave's half of O; the LSE from the first wave of the pair
+  // ---- epilogue: this wave's half of O; the LSE from the first wave of the pair. Causal: O
+  //      leaves through LDS as whole half-rows (see the hd128/hd256 kernel's epilogue): wave w
+  //      stages its 32 x 256 bf16 tile (16 KB) in half of K/V buffer w/2 (every wave is past
+  //      the last tile's barrier), 16-byte chunk k of row r at chunk k ^ (r mod 32), and reads
+  //      it back 16 bytes per lane (+1-3% at 8k-32k, +7% at 1k). Non-causal keeps direct
+  //      stores: with the staging its tile loop compiled 3-6% slower at 8k-32k.
   lL += other_half(lL);
   lO += other_half(lO);
-  if (q_lane < Nq) {
+  if constexpr (!CAUSAL) {
+    if (q_lane < Nq) {
+      const float inv = 1.0f / lO;
+      uint8_t* op = p.o + (((size_t)b * Nq + q_lane) * p.Hq + hq) * (size_t)(D * 2) + half * (DH * 2);
+#pragma unroll
+      for (int md = 0; md < MT2; ++md)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const x2 a = T::cvt2(acc[md][4 * i + 0] * inv, acc[md][4 * i + 1] * inv);
+          const x2 bb = T::cvt2(acc[md][4 * i + 2] * inv, acc[md][4 * i + 3] * inv);
+          u32x2 w;
+          w[0] = __builtin_bit_cast(unsigned, a);
+          w[1] = __builtin_bit_cast(unsigned, bb);
+          *(u32x2*)(op + (32 * md + 8 * i + 4 * hh) * 2) = w;
+        }
+    }
+  } else {
+    constexpr int RB = DH * 2, CPL = RB / 16, RPI = 64 / CPL;  // bytes, chunks per half-row; rows per read
+    static_assert(2 * 32 * RB <= C::KBUF && 2 * 32 * RB <= C::VBUF, "two staged tiles per K/V buffer");
+    const int ws = __builtin_amdgcn_readfirstlane(wave), wb = ws >> 1;
+    uint8_t* const ost = (wb == 0 ? k_lds0 : wb == 1 ? k_lds1 : wb == 2 ? v_lds0 : v_lds1) + (ws & 1) * (32 * RB);
     const float inv = 1.0f / lO;
-    uint8_t* op = p.o + (((size_t)b * Nq + q_lane) * p.Hq + hq) * (size_t)(D * 2) + half * (DH * 2);
 #pragma unroll
     for (int md = 0; md < MT2; ++md)
 #pragma unroll
@@ -294,11 +318,20 @@ fwd_hd512_kernel(FwdParams p) {
         u32x2 w;
         w[0] = __builtin_bit_cast(unsigned, a);
         w[1] = __builtin_bit_cast(unsigned, bb);
-        *(u32x2*)(op + (32 * md + 8 * i + 4 * hh) * 2) = w;
+        const int k = 4 * md + i;  // chunk of columns 32md + 8i .. +7 of this half; lane half at 8hh
+        *(u32x2*)(ost + l32 * RB + ((k ^ (l32 & (CPL - 1))) * 16) + 8 * hh) = w;
       }
-    if (hh == 0 && half == 0)
-      p.lse[((size_t)b * p.Hq + hq) * Nq + q_lane] = (m_run + __builtin_amdgcn_logf(lL)) * LN2;
+    const size_t o_row = (size_t)p.Hq * (D * 2);
+    uint8_t* const o0 = p.o + (((size_t)b * Nq + qw0) * p.Hq + hq) * (size_t)(D * 2) + half * RB;
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int r = it * RPI + lane / CPL, ch = lane % CPL;
+      const u32x4 v = *(const u32x4*)(ost + r * RB + ((ch ^ (r & (CPL - 1))) * 16));
+      if (qw0 + r < Nq) *(u32x4*)(o0 + r * o_row + ch * 16) = v;
+    }
   }
+  if (q_lane < Nq && hh == 0 && half == 0)
+    p.lse[((size_t)b * p.Hq + hq) * Nq + q_lane] = (m_run + __builtin_amdgcn_logf(lL)) * LN2;
 }
 
 }  // namespace fa
