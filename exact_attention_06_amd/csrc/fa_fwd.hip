@@ -189,7 +189,10 @@ int num_splits(int B, int Nq, int Nk, int Hq, int d, int causal) {
     s = 3;
   else if (blocks <= 512 && Nk >= 8192 && causal)
     s = 2;
-  return std::max(1, std::min(s, ntiles / 4));
+  // a workgroup costs about six key tiles of fixed work (prologue, first and last tile,
+  // stores): non-causal chunks keep at least 16 tiles, causal ones (whose diagonal tiles pile
+  // up on the last query tiles) at least 4
+  return std::max(1, std::min(s, ntiles / (causal ? 4 : 16)));
 }
 
 template <class T>

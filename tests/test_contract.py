@@ -259,6 +259,8 @@ def test_num_splits_choice():
     assert fa.num_splits(1, 2048, 2048, 8, 256) == 2                # 128 workgroups, 2k keys
     assert fa.num_splits(1, 4096, 4096, 8, 256) == 1
     assert fa.num_splits(1, 4096, 4096, 8, 256, causal=True) == 3
+    assert fa.num_splits(1, 1024, 1024, 16, 128) == 1               # 16 key tiles: too short to cut
+    assert fa.num_splits(1, 1024, 1024, 16, 128, causal=True) == 4
     for shape in [(1, 1024, 1024, 8, 256), (1, 1024, 1024, 16, 128), (2, 2048, 2048, 8, 256)]:
         s = fa.num_splits(*shape)
         assert 1 <= s <= 4
