@@ -79,14 +79,20 @@ template <int D> constexpr int bwd_kv_pf2() { return D == 128 ? 0 : 2; }
 
 // Load one BT-row tile of a [.., tokens, heads, D] tensor straight into LDS (padded rows).
 // `base` points at (b, token 0, head); rows past `valid_rows` load zeros.
-template <int D, int NW>
+template <int D, int NW, bool SCALAR_DESC>
 __device__ __forceinline__ void bwd_load_rows(const uint8_t* base, uint32_t row_bytes, int row0,
                                               int valid_rows, uint8_t* ldst, int wave, int lane) {
   using C = BwdCfg<D>;
   constexpr int SL = C::ROW / 16, CPR = D / 8;
   constexpr int NI = (C::BT * SL + 63) / 64;
   const int nv = valid_rows - row0 < C::BT ? valid_rows - row0 : C::BT;
-  const auto rs = make_rsrc(base + (size_t)row0 * row_bytes, (uint32_t)(nv > 0 ? nv : 0) * row_bytes);
+  // The clamp is computed on the VALU, so the descriptor lands in VGPRs and each load gets a
+  // waterfall loop unless readfirstlane keeps it scalar (SCALAR_DESC). That helps the dq
+  // kernels and the hd128 dk/dv kernel (backward hd128 +2% non-causal, +10% causal); the
+  // hd256 dk/dv kernel spilled with it (-4% / -12%) and keeps the loop.
+  const int nvc = nv > 0 ? nv : 0;
+  const uint32_t nrec = (uint32_t)(SCALAR_DESC ? __builtin_amdgcn_readfirstlane(nvc) : nvc) * row_bytes;
+  const auto rs = make_rsrc(base + (size_t)row0 * row_bytes, nrec);
 #pragma unroll
   for (int n = 0; n < (NI + NW - 1) / NW; ++n) {
     const int I = wave + NW * n;
@@ -164,14 +170,14 @@ bwd_dq_kernel(BwdParams p) {
   const int grp = lane >> 4, gi = lane & 15;
   const int t_rd = (4 * (grp >> 1) + (gi >> 2)) * ROW + (2 * (grp & 1) + ((gi & 3) >> 1)) * 16 + (gi & 1) * 8;
 
-  bwd_load_rows<D, NW>(kbase, kv_row, 0, Nk, k_lds[0], wv, lane);
-  bwd_load_rows<D, NW>(vbase, kv_row, 0, Nk, v_lds[0], wv, lane);
+  bwd_load_rows<D, NW, true>(kbase, kv_row, 0, Nk, k_lds[0], wv, lane);
+  bwd_load_rows<D, NW, true>(vbase, kv_row, 0, Nk, v_lds[0], wv, lane);
   __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
     if (j + 1 < ntiles) {
-      bwd_load_rows<D, NW>(kbase, kv_row, (j + 1) * BT, Nk, k_lds[buf ^ 1], wv, lane);
-      bwd_load_rows<D, NW>(vbase, kv_row, (j + 1) * BT, Nk, v_lds[buf ^ 1], wv, lane);
+      bwd_load_rows<D, NW, true>(kbase, kv_row, (j + 1) * BT, Nk, k_lds[buf ^ 1], wv, lane);
+      bwd_load_rows<D, NW, true>(vbase, kv_row, (j + 1) * BT, Nk, v_lds[buf ^ 1], wv, lane);
     }
     if (j < wtiles) {
       const uint8_t* kl = k_lds[buf];
@@ -321,8 +327,8 @@ bwd_dkdv_kernel(BwdParams p) {
     const int h = tile_head(n), q0 = tile_q0(n);
     const uint8_t* qb = p.q + ((size_t)b * Nq * p.Hq + h) * (size_t)(D * 2);
     const uint8_t* db = p.dout + ((size_t)b * Nq * p.Hq + h) * (size_t)(D * 2);
-    bwd_load_rows<D, NW>(qb, q_row, q0, Nq, q_lds[buf], wv, lane);
-    bwd_load_rows<D, NW>(db, q_row, q0, Nq, d_lds[buf], wv, lane);
+    bwd_load_rows<D, NW, D == 128>(qb, q_row, q0, Nq, q_lds[buf], wv, lane);
+    bwd_load_rows<D, NW, D == 128>(db, q_row, q0, Nq, d_lds[buf], wv, lane);
     if (wv == 0) {  // LSE and D of the tile's BT queries (zeros past Nq)
       const size_t lo = ((size_t)b * p.Hq + h) * Nq;
       const int nv = Nq - q0 < BT ? Nq - q0 : BT;
