@@ -119,7 +119,11 @@ bwd_dq_kernel(BwdParams p) {
   constexpr int PF1 = BWD_DQ_PF1, PF2 = BWD_DQ_PF2;
   static_assert(BT == 32, "one 32-key score tile per key tile");
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][C::TB], v_lds[2][C::TB];
+  // separate objects per buffer, and a buffer parity that is a literal in the loop: the
+  // compiler can then see that the direct-to-LDS loads of the next tile never alias the tile
+  // being read (with one [2][TB] array and j & 1 it waited for those loads at the top of
+  // every iteration; the dk/dv kernel keeps that form: unrolled the same way it spilled)
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds0[C::TB], k_lds1[C::TB], v_lds0[C::TB], v_lds1[C::TB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -170,18 +174,18 @@ bwd_dq_kernel(BwdParams p) {
   const int grp = lane >> 4, gi = lane & 15;
   const int t_rd = (4 * (grp >> 1) + (gi >> 2)) * ROW + (2 * (grp & 1) + ((gi & 3) >> 1)) * 16 + (gi & 1) * 8;
 
-  bwd_load_rows<D, NW, true>(kbase, kv_row, 0, Nk, k_lds[0], wv, lane);
-  bwd_load_rows<D, NW, true>(vbase, kv_row, 0, Nk, v_lds[0], wv, lane);
+  bwd_load_rows<D, NW, true>(kbase, kv_row, 0, Nk, k_lds0, wv, lane);
+  bwd_load_rows<D, NW, true>(vbase, kv_row, 0, Nk, v_lds0, wv, lane);
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
+  auto iteration = [&](const int j, auto par_tag) {
+    constexpr int PAR = decltype(par_tag)::value;  // j & 1
     if (j + 1 < ntiles) {
-      bwd_load_rows<D, NW, true>(kbase, kv_row, (j + 1) * BT, Nk, k_lds[buf ^ 1], wv, lane);
-      bwd_load_rows<D, NW, true>(vbase, kv_row, (j + 1) * BT, Nk, v_lds[buf ^ 1], wv, lane);
+      bwd_load_rows<D, NW, true>(kbase, kv_row, (j + 1) * BT, Nk, PAR ? k_lds0 : k_lds1, wv, lane);
+      bwd_load_rows<D, NW, true>(vbase, kv_row, (j + 1) * BT, Nk, PAR ? v_lds0 : v_lds1, wv, lane);
     }
     if (j < wtiles) {
-      const uint8_t* kl = k_lds[buf];
-      const uint8_t* vl = v_lds[buf];
+      const uint8_t* kl = PAR ? k_lds1 : k_lds0;
+      const uint8_t* vl = PAR ? v_lds1 : v_lds0;
       // S^T and dP^T, each as two alternating accumulators over the head dim
       f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
       {
@@ -243,7 +247,13 @@ bwd_dq_kernel(BwdParams p) {
       }
     }
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    iteration(j, IntC<0>{});
+    iteration(j + 1, IntC<1>{});
   }
+  if (j < ntiles) iteration(j, IntC<0>{});
 
   if (q_lane < Nq) {
     uint8_t* op = p.dq + (((size_t)b * Nq + q_lane) * p.Hq + hq) * (size_t)(D * 2);
