@@ -832,6 +832,10 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
     __builtin_amdgcn_sched_barrier(0);
+    // Wave priority by progress: the two waves that share a SIMD meet at every tile barrier,
+    // and the issue arbiter otherwise favours the older one, which then waits at the barrier
+    // while the younger finishes alone. A wave in phase 1 outranks one already in phase 2.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < N1; ++i) {
       if (i + PF < N1)
@@ -858,6 +862,7 @@ fwd_kernel(FwdParams p) {
     }
     float mx = -__builtin_inff();
     constexpr int VPS = (16 * MT1) / N2;  // p values summed (and next-tile scores maxed) per step
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < N2; ++i) {
       if (i + PF < N2) vf[i + PF] = vfrag(i + PF);
