@@ -58,6 +58,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Lazy-rescale threshold in log2 units: p = exp2(s*c - m) stays <= 2^TAU between rescales.
 constexpr float TAU = 8.0f;
+// The first K/V tile of a block feeds P as hi + lo (two bf16 MFMAs, ~16 significant bits):
+// for rows that see few keys the bf16 rounding of P is a visible part of the O error. In the
+// hd128 loop only when some row of the block sees fewer keys than this in the block's key
+// range (rows with more keys average that rounding out), and the first tile otherwise takes
+// the scheduled main iteration; the hd256 loop always splits its first tile (a second
+// first-tile form in that loop made it slower).
+constexpr int P_SPLIT_KEYS = 512;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -395,6 +402,9 @@ fwd_kernel(FwdParams p) {
   const int wtiles = max(0, min(wtiles_all, t1) - t0);
   const int nfull = max(0, min(nfull_all, t1) - t0);
   const int kfirst = t0 * BC;  // first key of the range
+  // fewest keys a row of this block sees in the range: below P_SPLIT_KEYS the first tile of
+  // the hd128 loop feeds P as hi + lo
+  const bool split_first = min(CAUSAL ? min(Nk, q_wg0 + cshift + 1) : Nk, t1 * BC) - kfirst < P_SPLIT_KEYS;
   // row of (split, this head, query q_lane) in the split-KV partials: dense [splits, B*Hq, Nq],
   // variable-length [splits, Hq, total_q] (packed query rows)
   auto part_row = [&](int ql) -> size_t {
@@ -891,7 +901,12 @@ fwd_kernel(FwdParams p) {
   using T1 = BoolC<true>;
   int j = 0;
   if (nmain > 0) {
-    iteration(0, s_a, s_b, T1{}, T0{});
+    if (split_first) {
+      iteration(0, s_a, s_b, T1{}, T0{});
+    } else {
+      mt_cur = rowmax(s_a);
+      main_iteration(0, s_a, s_b, IntC<0>{});
+    }
     j = 1;
     for (; j + 1 < nmain; j += 2) {
       main_iteration(j, s_b, s_a, IntC<1>{});

@@ -113,6 +113,26 @@ def test_rectangular_noncausal(case):
     _run_full(name, B, Nq, Nk, Hq, Hkv, d, False, seed)
 
 
+# The hd128 loop feeds the first tile's P as hi + lo only when some row of the block sees
+# fewer than 512 keys of its range. These shapes sit on both sides of that bound: key counts
+# 511 / 512 / 513 non-causal, and causal N = 768, whose query tiles of 256 rows start at
+# 1, 257 and 513 visible keys (two tiles split, one not), plain and with spiked keys.
+THRESH = [
+    ("nk511", 1, 300, 511, 4, 2, False, 41, False),
+    ("nk512", 1, 300, 512, 4, 2, False, 42, False),
+    ("nk513", 1, 300, 513, 4, 2, False, 43, False),
+    ("nk512_spiked", 1, 300, 512, 4, 4, False, 44, True),
+    ("causal768", 1, 768, 768, 4, 2, True, 45, False),
+    ("causal768_spiked", 1, 768, 768, 4, 4, True, 46, True),
+]
+
+
+@pytest.mark.parametrize("case", THRESH, ids=[c[0] for c in THRESH])
+def test_first_tile_split_bound(case):
+    name, B, Nq, Nk, Hq, Hkv, causal, seed, spiked = case
+    _run_full(name, B, Nq, Nk, Hq, Hkv, 128, causal, seed, k_spike=spiked)
+
+
 @pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
 @pytest.mark.parametrize("d", [128, 256, 512])
 def test_fp16_entry_point(d, causal):
