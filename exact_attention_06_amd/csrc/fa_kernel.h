@@ -273,10 +273,13 @@ struct Layout {
   static constexpr int KT = BC * KROW;         // bytes per K tile
   static constexpr int VT = BC * VROW;         // bytes per V tile
   // A tile is written by 64-slot (1 KB) direct-to-LDS loads spread evenly over the NL
-  // loading waves; each buffer is rounded up so that every loading wave issues the same
-  // number of whole loads (the slots past the tile receive zeros), which keeps the load
-  // code free of branches.
-  static constexpr int NL = NW;
+  // loading waves, waves LB .. LB + NL - 1; each buffer is rounded up so that every loading
+  // wave issues the same number of whole loads (the slots past the tile receive zeros).
+  // hd128: the four younger waves load (5 loads each per tile and buffers of 20 KB, against
+  // 3 per wave for all eight and 24 KB buffers); they are the ones that lag at the tile
+  // barriers, and the loads at the top of an iteration let the older waves run on.
+  static constexpr int NL = D == 128 ? NW / 2 : NW;
+  static constexpr int LB = NW - NL;
   static constexpr int KPW = (KT / 16 + 64 * NL - 1) / (64 * NL);  // K loads per loading wave
   static constexpr int VPW = (VT / 16 + 64 * NL - 1) / (64 * NL);  // V loads per loading wave
   static constexpr int KBUF = KPW * NL * 1024, VBUF = VPW * NL * 1024;
@@ -481,7 +484,7 @@ fwd_kernel(FwdParams p) {
   constexpr int NL = L::NL, KPW = L::KPW, VPW = L::VPW;  // loading waves, loads per wave and tile
   constexpr uint32_t OOB = 0x80000000u;
   const uint32_t kv_row = (uint32_t)p.Hkv * D * 2;  // bytes between consecutive tokens
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wv = __builtin_amdgcn_readfirstlane(wave) - L::LB;  // index among the loading waves
   uint32_t k_vo[KPW], v_vo[VPW];
 #pragma unroll
   for (int n = 0; n < KPW; ++n) {
@@ -497,6 +500,7 @@ fwd_kernel(FwdParams p) {
   auto load_tile = [&](int tile, const uint8_t* gbase, uint8_t* ldst, const uint32_t* vo,
                        auto nw_tag) {
     constexpr int NPW = decltype(nw_tag)::value;
+    if (NL < NW && (wv < 0 || wv >= NL)) return;  // not a loading wave
     const int k0 = (t0 + tile) * BC;
     const uint8_t* tbase = gbase + (size_t)k0 * kv_row;
     int rows = min(BC, Nk - k0);
