@@ -97,11 +97,16 @@ def cpu_baseline(w, causal, budget_s=12.0):
     from exact_attention_06_amd import workloads as W
     from oracle import attention_ref
 
+    # the host cores this process may run on; the BLAS pool behind numpy is set to that many
+    # threads for the timed oracle calls
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+                           or [cores])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        limiter, blas_threads = None, cores
     R = 256
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed + 200)
@@ -130,7 +135,10 @@ def cpu_baseline(w, causal, budget_s=12.0):
                     break
             if dt > budget_s:
                 break
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(cores), "blas_threads": int(blas_threads),
+            "kind": "oracle",
             "sample": f"{done_rows} random query rows ({R} per (batch, head), {heads} (batch, head) visits) of {w.name} "
                       f"{'causal' if causal else 'non-causal'} with all {w.N} keys, fp64 numpy oracle; "
                       f"{dt:.1f} s of CPU work; FLOPs 4*d per visible key per row"}
@@ -413,7 +421,8 @@ def main():
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, causal)
     if cpu:
-        log(f"[cpu] oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['sample']})")
+        log(f"[cpu] oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} cores, {cpu['blas_threads']} BLAS "
+            f"threads ({cpu['sample']})")
 
     kname = f"fwd_kernel<{w.d},{'causal' if causal else 'noncausal'},bf16>"
     # counter figures from the same committed profile as `traffic` (null when stale): the shader

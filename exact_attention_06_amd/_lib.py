@@ -52,12 +52,14 @@ _PAGED_SPLIT_ARGS = [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _I, _I
 
 
 def load():
-    """Load libfa.so once; raise if it has not been built."""
+    """Load libfa.so once; raise if it has not been built. FA_LIB may name another build of
+    the same sources (the host-only AddressSanitizer build runs the contract tests)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_attention_06_amd.build`")
-        lib = ctypes.CDLL(LIB_PATH)
+        path = os.environ.get("FA_LIB") or LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m exact_attention_06_amd.build`")
+        lib = ctypes.CDLL(path)
         for name in ("fa_fwd", "fa_fwd_f16"):
             fn = getattr(lib, name)
             fn.argtypes = _FWD_ARGS

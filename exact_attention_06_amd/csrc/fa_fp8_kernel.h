@@ -94,6 +94,8 @@ fwd_fp8_kernel(FwdParams p) {
         qf[t][e] = (int)lo[e];
         qf[t][4 + e] = (int)hi[e];
       }
+      if (p.neg_scores)  // negative scale: -Q (e4m3 sign bit 7 of every byte, exact)
+        for (int e = 0; e < 8; ++e) qf[t][e] ^= (int)0x80808080u;
       if (p.zero_scores) qf[t] = i32x8{};
     }
   }

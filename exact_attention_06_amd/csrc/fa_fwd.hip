@@ -37,11 +37,16 @@ int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
   return FA_OK;
 }
 
-// Scale: a zero (or subnormal) scale makes every visible score exactly 0; the kernel then
-// zeroes Q and uses c = log2(e), since -inf * 0 would turn masked scores into NaN.
-void set_scale(fa::FwdParams& prm, float scale) {
-  prm.zero_scores = !(scale * fa::LOG2E >= FLT_MIN);
-  prm.c = prm.zero_scores ? fa::LOG2E : scale * fa::LOG2E;
+// Scale: the kernels take c = |scale| * log2(e) > 0 (the row maximum relies on c >= 0). A
+// negative scale flips the sign of Q instead (exact: |scale| (-q).k == scale q.k bit for bit).
+// A zero (or subnormal) scale makes every visible score exactly 0; the kernel then zeroes Q
+// and uses c = log2(e), since -inf * 0 would turn masked scores into NaN.
+template <class P>
+void set_scale(P& prm, float scale) {
+  const float a = std::fabs(scale) * fa::LOG2E;
+  prm.zero_scores = !(a >= FLT_MIN);
+  prm.neg_scores = scale < 0.f && !prm.zero_scores;
+  prm.c = prm.zero_scores ? fa::LOG2E : a;
 }
 
 template <int VM, class T>
@@ -76,7 +81,7 @@ int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, fl
   if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 128 && d != 256) return FA_ERR_HEADDIM;
   if (causal && Nq != Nk) return FA_ERR_CAUSAL_SHAPE;
-  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
   for (float x : {q_scale, k_scale, v_scale})
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
@@ -98,9 +103,7 @@ int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, fl
   prm.Hkv = Hkv;
   prm.group = Hq / Hkv;
   clear_extras(prm);
-  const float c = scale * q_scale * k_scale * fa::LOG2E;
-  prm.zero_scores = !(c >= FLT_MIN);
-  prm.c = prm.zero_scores ? fa::LOG2E : c;
+  set_scale(prm, scale * q_scale * k_scale);
   prm.v_scale = v_scale;
   prm.nqt = (Nq + (int)BR - 1) / (int)BR;
   hipStream_t s = (hipStream_t)stream;
@@ -117,7 +120,7 @@ int check(const void* q, const void* k, const void* v, const void* o, const floa
   if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 128 && d != 256 && !(hd512 && d == 512)) return FA_ERR_HEADDIM;
   if (causal && Nq != Nk) return FA_ERR_CAUSAL_SHAPE;
-  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
   if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
   const int64_t BR = d == 128 ? br<128>() : d == 256 ? br<256>() : fa::Hd512::BR;
@@ -241,7 +244,7 @@ int check_var(const void* q, const void* k, const void* v, const void* o, const 
                 (int64_t)max_pages * page_size > INT_MAX || (int64_t)num_pages * page_size > INT_MAX))
     return FA_ERR_PAGE;
   if (d != 128 && d != 256) return FA_ERR_HEADDIM;
-  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
   if (((uintptr_t)lse | (uintptr_t)cu_q | (uintptr_t)cu_k | (uintptr_t)seqused | (uintptr_t)block_table) & 3)
     return FA_ERR_ALIGN;
@@ -375,8 +378,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   prm.Hkv = Hkv;
   prm.group = Hq / Hkv;
   prm.ntile = 0;
-  prm.zero_scores = !(scale * fa::LOG2E >= FLT_MIN);  // as in the forward pass
-  prm.c = prm.zero_scores ? fa::LOG2E : scale * fa::LOG2E;
+  set_scale(prm, scale);  // as in the forward pass
   prm.scale = scale;
   hipStream_t s = (hipStream_t)stream;
   if (d == 128)
@@ -536,7 +538,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_SHAPE: return "B, Nq, Nk, Hq and Hkv must be positive and Hq a multiple of Hkv";
     case FA_ERR_HEADDIM: return "head dim must be 128 or 256 (or 512 for fa_fwd / fa_fwd_f16)";
     case FA_ERR_CAUSAL_SHAPE: return "causal attention needs Nq == Nk";
-    case FA_ERR_SCALE: return "scale must be finite and non-negative (fp8 dequantisation factors finite and positive)";
+    case FA_ERR_SCALE: return "scale must be finite (fp8 dequantisation factors finite and positive)";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_TOO_LARGE: return "problem too large for 32-bit grid or sequence indexing";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";

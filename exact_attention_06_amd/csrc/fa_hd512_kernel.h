@@ -83,6 +83,10 @@ fwd_hd512_kernel(FwdParams p) {
 #pragma unroll
       for (int t = 0; t < KS1; ++t) qf[t] = x8{};
     }
+    if (p.neg_scores) {  // negative scale: -Q (exact) with c = |scale| * log2(e)
+#pragma unroll
+      for (int t = 0; t < KS1; ++t) qf[t] = negate16(qf[t]);
+    }
   }
 
   f32x16 acc[MT2];

@@ -129,8 +129,9 @@ struct FwdParams {
   int B, Nq, Nk, Hq, Hkv;
   int group;      // Hq / Hkv
   int nqt;        // query tiles per (b, h)
-  float c;        // scale * log2(e); log2(e) when zero_scores is set
+  float c;        // |scale| * log2(e); log2(e) when zero_scores is set
   int zero_scores;  // scale is zero (or below the normal range): every score is exactly 0
+  int neg_scores;   // scale < 0: Q enters with its sign flipped (exact), so c stays positive
   // variable-length batches (kernel variant VAR): packed q/o rows of sequence b are
   // cu_q[b] .. cu_q[b+1]-1; keys are packed rows cu_k[b] .. cu_k[b+1]-1 or, with a page
   // table, logical key t of sequence b is row t % page_size of page
@@ -155,6 +156,16 @@ struct FwdParams {
 
 template <bool V> struct BoolC { static constexpr bool value = V; };
 template <int V> struct IntC { static constexpr int value = V; };
+
+// Sign flip of every 16-bit element of a fragment (bf16 / fp16: bit 15). Exact, so that
+// |scale| * (-q) . k equals scale * q . k bit for bit and c = |scale| * log2(e) stays >= 0,
+// which the row maximum relies on (max(s) * c == max(s * c)).
+template <class X8>
+__device__ __forceinline__ X8 negate16(X8 x) {
+  u32x4 u = __builtin_bit_cast(u32x4, x);
+  u ^= 0x80008000u;
+  return __builtin_bit_cast(X8, u);
+}
 
 // Lane l and lane l^32 hold the same query row: the value of the other half.
 __device__ __forceinline__ float other_half(float x) {
@@ -447,10 +458,15 @@ fwd_kernel(FwdParams p) {
       u32x4 raw = *(const u32x4*)(qp + (16 * t + 8 * hh) * 2);
       qf[t] = __builtin_bit_cast(x8, raw);
     }
-    // zero scale: zero Q (and a unit c), so that masked scores stay -inf instead of -inf * 0
+    // zero scale: zero Q (and a unit c), so that masked scores stay -inf instead of -inf * 0;
+    // negative scale: -Q with c = |scale| * log2(e)
     if (p.zero_scores) {
 #pragma unroll
       for (int t = 0; t < KS1; ++t) qf[t] = x8{};
+    }
+    if (p.neg_scores) {
+#pragma unroll
+      for (int t = 0; t < KS1; ++t) qf[t] = negate16(qf[t]);
     }
   }
 
@@ -646,7 +662,8 @@ fwd_kernel(FwdParams p) {
     }
   };
 
-  // Row max of a tile in log2 units (c >= 0, so max(s)*c == max(s*c)), over both lane halves.
+  // Row max of a tile in log2 units (c >= 0 always: a negative scale flips the sign of Q
+  // instead, so max(s)*c == max(s*c)), over both lane halves.
   auto rowmax = [&](const f32x16 (&s)[MT1]) -> float {
     float mx = s[0][0];
 #pragma unroll

@@ -54,7 +54,7 @@ enum fa_status {
   FA_ERR_HEADDIM = -3,      /* d is not 128 or 256 (fa_fwd and fa_fwd_f16: or 512)         */
   FA_ERR_CAUSAL_SHAPE = -4, /* causal with Nq != Nk (the causal alignment is defined for
                                square problems only)                                       */
-  FA_ERR_SCALE = -5,        /* scale is NaN, infinite or negative                          */
+  FA_ERR_SCALE = -5,        /* scale is NaN or infinite                                    */
   FA_ERR_ALIGN = -6,        /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_TOO_LARGE = -7,    /* the work grid or a per-head extent exceeds 2^31 - 1         */
   FA_ERR_LAUNCH = -8,       /* the HIP launch reported an error                            */
@@ -66,8 +66,9 @@ enum fa_status {
 };
 
 /* Forward pass, bf16 q/k/v/o, fp32 LSE. Arguments as described above; `scale` multiplies
- * the q.k dot products (1/sqrt(d) is the usual choice). d is 128, 256 or 512. Returns an
- * fa_status. */
+ * the q.k dot products (1/sqrt(d) is the usual choice; any finite value is accepted: zero
+ * gives uniform weights over the visible keys, a negative scale scores of the opposite
+ * sign). d is 128, 256 or 512. Returns an fa_status. */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
            void* stream);

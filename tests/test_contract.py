@@ -50,6 +50,9 @@ def test_valid_arguments_pass():
     assert _check(Nq=1, Nk=1) == _lib.FA_OK
     assert _check(Nq=5, Nk=9000) == _lib.FA_OK
     assert _check(scale=0.0) == _lib.FA_OK
+    # a negative scale is a valid softmax(scale * Q K^T) (scores of the opposite sign)
+    assert _check(scale=-0.0884) == _lib.FA_OK
+    assert _check(scale=-1e30) == _lib.FA_OK
 
 
 @pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
@@ -87,7 +90,7 @@ def test_causal_needs_square():
     assert _check(causal=0, Nq=300, Nk=301) == _lib.FA_OK
 
 
-@pytest.mark.parametrize("s", [math.inf, -math.inf, math.nan, -0.5])
+@pytest.mark.parametrize("s", [math.inf, -math.inf, math.nan, -math.nan])
 def test_bad_scale(s):
     assert _check(scale=s) == _lib.FA_ERR_SCALE
 
@@ -213,7 +216,7 @@ def test_paged_rejects_before_any_hip_call(entry):
                dict(max_pages=0), dict(max_pages=1 << 24), dict(num_pages=1 << 24)):
         assert _paged(fn, **kw) == _lib.FA_ERR_PAGE, kw
     assert _paged(fn, d=64) == _lib.FA_ERR_HEADDIM
-    assert _paged(fn, scale=-1.0) == _lib.FA_ERR_SCALE
+    assert _paged(fn, scale=-math.inf) == _lib.FA_ERR_SCALE
     for kw in (dict(k=A + 8), dict(bt=A + 2), dict(used=A + 1)):
         assert _paged(fn, **kw) == _lib.FA_ERR_ALIGN, kw
 

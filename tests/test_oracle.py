@@ -157,22 +157,27 @@ def test_heads_and_batches_independent():
 # --- a second formulation and a library routine
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_matches_bruteforce_fsum(causal):
+@pytest.mark.parametrize("scale", [0.45, -0.45], ids=["pos", "neg"])
+def test_matches_bruteforce_fsum(causal, scale):
     q, k, v = _rand(2, 7, 4, 2, 5, 11)
-    O0, L0 = attention_ref(q, k, v, causal, 0.45)
-    O1, L1 = attention_bruteforce(q, k, v, causal, 0.45)
+    O0, L0 = attention_ref(q, k, v, causal, scale)
+    O1, L1 = attention_bruteforce(q, k, v, causal, scale)
     np.testing.assert_allclose(O0, O1, rtol=0, atol=1e-14)
     np.testing.assert_allclose(L0, L1, rtol=0, atol=1e-14)
 
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("hkv", [4, 2])
-def test_matches_torch_sdpa_fp64(causal, hkv):
+@pytest.mark.parametrize("scale", [0.3, -0.3], ids=["pos", "neg"])
+def test_matches_torch_sdpa_fp64(causal, hkv, scale):
+    # a negative scale is an ordinary softmax(scale * Q K^T) with scores of the opposite sign
     q, k, v = _rand(2, 16, 4, hkv, 8, 12)
-    scale = 0.3
     O0, L0 = attention_ref(q, k, v, causal, scale)
     tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))  # -> [B, H, N, d]
-    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale,
+    # torch's math path multiplies q and k by sqrt(scale) each, so a negative scale goes in
+    # as |scale| with -q (the same scores, exactly)
+    sq = tq if scale > 0 else -tq
+    out = torch.nn.functional.scaled_dot_product_attention(sq, tk, tv, is_causal=causal, scale=abs(scale),
                                                            enable_gqa=hkv != 4)
     np.testing.assert_allclose(O0, out.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-14)
     # LSE through torch.logsumexp over the masked score matrix

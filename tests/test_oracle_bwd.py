@@ -16,12 +16,15 @@ def _rand(B, N, Hq, Hkv, d, seed, Nk=None):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("hkv", [4, 2, 1])
-def test_matches_torch_autograd_fp64(causal, hkv):
+@pytest.mark.parametrize("scale", [0.37, -0.37], ids=["pos", "neg"])
+def test_matches_torch_autograd_fp64(causal, hkv, scale):
     q, k, v, do = _rand(2, 9, 4, hkv, 6, 1)
-    scale = 0.37
     dq, dk, dv = attention_bwd_ref(q, k, v, do, causal, scale)
     tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3).requires_grad_(True) for x in (q, k, v))
-    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale,
+    # torch's math path multiplies q and k by sqrt(scale) each: a negative scale goes in as
+    # |scale| with -q (the same scores); the chain rule then flips the sign of dq
+    sgn = 1.0 if scale > 0 else -1.0
+    out = torch.nn.functional.scaled_dot_product_attention(sgn * tq, tk, tv, is_causal=causal, scale=abs(scale),
                                                            enable_gqa=hkv != 4)
     out.backward(torch.from_numpy(do).permute(0, 2, 1, 3))
     for mine, t in ((dq, tq), (dk, tk), (dv, tv)):

@@ -16,6 +16,8 @@ import exact_attention_06_amd as fa
 from exact_attention_06_amd import workloads as W
 from oracle import attention_ref
 
+from parity_record import record
+
 pytestmark = pytest.mark.gpu
 
 O_MAX, O_MEAN, LSE_MAX = 1e-2, 1e-3, 1e-3
@@ -56,6 +58,7 @@ def _compare(name, o, lse, O_ref, L_ref, rows=None):
     ex_big = float(excess[big].max()) if big.any() else 0.0
     _say(f"  {name}: O max {mx:.3e} (|O|<4: {mx_small:.3e}) mean {mean:.3e} | LSE max {lmx:.3e}"
          f" | |O_ref|>=4: {int(big.sum())} elems, max excess over half-ulp {ex_big:.3e}")
+    record(case=name, o_max=mx, o_max_small=mx_small, o_mean=mean, lse_max=lmx, n_big=int(big.sum()), ex_big=ex_big)
     assert mx_small <= O_MAX and ex_big <= EXCESS and mean <= O_MEAN and lmx <= LSE_MAX, \
         f"{name}: O max {mx:.3e} (|O|<4 {mx_small:.3e}, excess {ex_big:.3e}) mean {mean:.3e} LSE max {lmx:.3e}"
 
@@ -174,6 +177,28 @@ def test_hot_scores(d, causal):
     _run_full(f"hot_scores_d{d}", 1, 600, 600, 2, 1, d, causal, 80 + d, scale=1.0)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_negative_scale(d, causal):
+    # scale -1/sqrt(d): a valid softmax over scores of the opposite sign (the kernels flip
+    # the sign of Q and keep c = |scale| log2(e)); 600 tokens span several tiles and a tail
+    _run_full(f"neg_scale_d{d}", 2, 600, 600, 4, 2, d, causal, 90 + d, scale=-float(d) ** -0.5)
+
+
+def test_negative_scale_full_size_sampled_rows():
+    # the benchmark's hd256 N = 8192 launch with scale -1/16, on sampled rows
+    w = W.by_name("hd256_N8192")
+    q, k, v = W.inputs_for(w)
+    rows = W.sample_rows(w.B, w.Hq, w.N, w.seed).numpy()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for causal in (False, True):
+        _say(f"[gpu] {w.name} scale={-w.scale} causal={causal}")
+        o, lse = fa.forward(qd, kd, vd, causal=causal, scale=-w.scale)
+        torch.cuda.synchronize()
+        O_ref, L_ref = attention_ref(q, k, v, causal, -w.scale, rows=rows)
+        _compare(f"{w.name}/neg_scale/{'causal' if causal else 'noncausal'}", o, lse, O_ref, L_ref, rows=rows)
+
+
 @pytest.mark.parametrize("w", [W.tiny(), W.ragged()], ids=["tiny", "ragged"])
 def test_named_small_workloads(w):
     for causal in w.causal_modes:
@@ -264,6 +289,15 @@ def test_splitkv_one_split_equals_plain_bitwise(d):
         o2, l2 = fa.forward_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=causal, num_splits=1)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2), (d, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+def test_splitkv_negative_scale(causal):
+    q, k, v = W.make_qkv(1, 777, 777, 4, 2, 128, 98)
+    o, lse = fa.forward_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=-0.125, num_splits=3)
+    torch.cuda.synchronize()
+    O_ref, L_ref = attention_ref(q, k, v, causal, -0.125)
+    _compare("splitkv_neg_scale", o, lse, O_ref, L_ref)
 
 
 def test_splitkv_fp16():

@@ -26,28 +26,8 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _run(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, head=None, scale=None):
-    """head=(b, kvh): compare only that KV head's group (dq of its query heads, its dk, dv)."""
-    q, k, v = W.make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, dtype=dtype)
-    g = torch.Generator().manual_seed(seed + 7)
-    do = torch.randn((B, Nq, Hq, d), generator=g).to(dtype)
-    if scale is None:
-        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
-    _say(f"[gpu] bwd {name} B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} {dtype}")
-    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
-    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
-    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
-    torch.cuda.synchronize()
-    if head is not None:
-        b, kvh = head
-        gsz = Hq // Hkv
-        hs = slice(kvh * gsz, (kvh + 1) * gsz)
-        rq, rk, rv = attention_bwd_ref(q[b:b + 1, :, hs], k[b:b + 1, :, kvh:kvh + 1], v[b:b + 1, :, kvh:kvh + 1],
-                                       do[b:b + 1, :, hs], causal, scale)
-        dq, dk, dv = dq[b:b + 1, :, hs], dk[b:b + 1, :, kvh:kvh + 1], dv[b:b + 1, :, kvh:kvh + 1]
-    else:
-        rq, rk, rv = attention_bwd_ref(q, k, v, do, causal, scale)
-    for tname, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+def _compare(name, got_all, ref_all):
+    for tname, got, ref in zip(("dq", "dk", "dv"), got_all, ref_all):
         got = got.float().cpu().numpy().astype(np.float64)
         assert np.isfinite(got).all(), f"{name}/{tname}: non-finite"
         err = np.abs(got - ref)
@@ -58,6 +38,31 @@ def _run(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, head=N
             assert mx == 0.0, f"{name}/{tname}"
             continue
         assert mx <= MAX_REL * rmax and mean <= MEAN_REL * rmean, f"{name}/{tname}"
+
+
+def _run(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, heads=None, scale=None):
+    """heads=[(b, kvh), ...]: compare only those KV heads' groups (dq of their query heads,
+    their dk and dv), each against its own oracle call."""
+    q, k, v = W.make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, dtype=dtype)
+    g = torch.Generator().manual_seed(seed + 7)
+    do = torch.randn((B, Nq, Hq, d), generator=g).to(dtype)
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    _say(f"[gpu] bwd {name} B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} {dtype} scale={scale}")
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    if heads is None:
+        _compare(name, (dq, dk, dv), attention_bwd_ref(q, k, v, do, causal, scale))
+        return
+    gsz = Hq // Hkv
+    for b, kvh in heads:
+        hs = slice(kvh * gsz, (kvh + 1) * gsz)
+        ref = attention_bwd_ref(q[b:b + 1, :, hs], k[b:b + 1, :, kvh:kvh + 1], v[b:b + 1, :, kvh:kvh + 1],
+                                do[b:b + 1, :, hs], causal, scale)
+        got = (dq[b:b + 1, :, hs], dk[b:b + 1, :, kvh:kvh + 1], dv[b:b + 1, :, kvh:kvh + 1])
+        _compare(f"{name}[b={b},kvh={kvh}]", got, ref)
 
 
 CASES = [
@@ -101,9 +106,18 @@ FULL_BWD = [W.by_name(n) for n in ("hd128_N8192_mha", "hd128_N8192_gqa4", "hd256
 
 @pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
 @pytest.mark.parametrize("w", FULL_BWD, ids=[w.name for w in FULL_BWD])
-def test_bwd_full_size_one_head(w, causal):
-    # full-size launch; the oracle covers KV head 0 of the last batch (and its query heads)
-    _run(w.name, w.B, w.N, w.N, w.Hq, w.Hkv, w.d, causal, w.seed, head=(w.B - 1, 0))
+def test_bwd_full_size_two_heads(w, causal):
+    # full-size launch; the oracle covers two KV-head groups in different batches: KV head 0
+    # of the last batch and the last KV head of the first batch (with their query heads)
+    _run(w.name, w.B, w.N, w.N, w.Hq, w.Hkv, w.d, causal, w.seed, heads=[(w.B - 1, 0), (0, w.Hkv - 1)])
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_negative_scale(d, causal):
+    # scale -1/sqrt(d): scores of the opposite sign; dq = scale dS K and dk = scale dS^T Q
+    # carry the sign
+    _run(f"neg_scale_d{d}", 2, 300, 300, 4, 2, d, causal, 90 + d, scale=-float(d) ** -0.5)
 
 
 def _random_case(i):

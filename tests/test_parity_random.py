@@ -11,6 +11,8 @@ import exact_attention_06_amd as fa
 from exact_attention_06_amd import workloads as W
 from oracle import attention_ref
 
+from parity_record import record
+
 pytestmark = pytest.mark.gpu
 
 O_MAX, O_MEAN, LSE_MAX = 1e-2, 1e-3, 1e-3
@@ -57,4 +59,8 @@ def test_random_shape(c):
     ex_big = float((eo - half_ulp)[big].max()) if big.any() else 0.0
     lmx = float(np.abs(lg - L_ref).max())
     print(f"  O max {eo.max():.3e} mean {eo.mean():.3e} LSE max {lmx:.3e}", flush=True)
+    tag = "B{B} Nq{Nq} Nk{Nk} Hq{Hq} Hkv{Hkv} d{d} {c} {t}".format(
+        **c, c="causal" if c["causal"] else "noncausal", t="bf16" if c["dtype"] == torch.bfloat16 else "fp16")
+    record(case=f"random {tag}", o_max=float(eo.max()), o_max_small=mx_small, o_mean=float(eo.mean()),
+           lse_max=lmx, n_big=int(big.sum()), ex_big=ex_big)
     assert mx_small <= O_MAX and ex_big <= EXCESS and eo.mean() <= O_MEAN and lmx <= LSE_MAX

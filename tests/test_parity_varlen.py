@@ -17,6 +17,8 @@ import exact_attention_06_amd as fa
 from exact_attention_06_amd import workloads as W
 from oracle import attention_paged_ref, attention_varlen_ref
 
+from parity_record import record
+
 pytestmark = pytest.mark.gpu
 
 O_MAX, O_MEAN, LSE_MAX = 1e-2, 1e-3, 1e-3
@@ -45,6 +47,7 @@ def _compare(name, o, lse, O_ref, L_ref):
     at = np.unravel_index(int(np.argmax(eo)), eo.shape)
     _say(f"  {name}: O max {mx:.3e} (|O_ref| there {abs(O_ref[at]):.3f}) mean {mean:.3e} | LSE max {lmx:.3e} | "
          f"|O_ref|>=4: {int(big.sum())} elems, excess {ex_big:.3e} | empty rows (x heads) {n_empty}")
+    record(case=name, o_max=mx, o_max_small=mx_small, o_mean=mean, lse_max=lmx, n_big=int(big.sum()), ex_big=ex_big)
     if n_empty:
         rows_empty = empty_ref.any(axis=0)
         assert np.all(o[rows_empty] == 0.0), f"{name}: empty rows must be exactly 0"
@@ -52,9 +55,10 @@ def _compare(name, o, lse, O_ref, L_ref):
         f"{name}: O max {mx:.3e} (|O|<4 {mx_small:.3e}, excess {ex_big:.3e}) mean {mean:.3e} LSE max {lmx:.3e}"
 
 
-def _run_varlen(name, Lq, Lk, Hq, Hkv, d, causal, seed, used=None, dtype=torch.bfloat16, splits=0):
+def _run_varlen(name, Lq, Lk, Hq, Hkv, d, causal, seed, used=None, dtype=torch.bfloat16, splits=0, scale=None):
     q, k, v, cu_q, cu_k = W.make_varlen(Lq, Lk, Hq, Hkv, d, seed, dtype)
-    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
     _say(f"[gpu] varlen {name} B={len(Lq)} Lq={list(Lq)[:8]} Lk={list(Lk)[:8]} used={used} Hq={Hq} "
          f"Hkv={Hkv} d={d} causal={causal} {dtype} splits={splits}")
     used_t = None if used is None else torch.tensor(used, dtype=torch.int32)
@@ -65,9 +69,10 @@ def _run_varlen(name, Lq, Lk, Hq, Hkv, d, causal, seed, used=None, dtype=torch.b
     _compare(name, o, lse, O_ref, L_ref)
 
 
-def _run_paged(name, Lq, used, page_size, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, splits=0):
+def _run_paged(name, Lq, used, page_size, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, splits=0, scale=None):
     q, kc, vc, cu_q, used_t, bt = W.make_paged(Lq, used, page_size, Hq, Hkv, d, seed, dtype)
-    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
     _say(f"[gpu] paged {name} B={len(Lq)} Lq={list(Lq)[:8]} used={list(used)[:8]} page={page_size} "
          f"pages={kc.shape[0]} Hq={Hq} Hkv={Hkv} d={d} causal={causal} {dtype} splits={splits}")
     o, lse = fa.forward_paged(q.cuda(), kc.cuda(), vc.cuda(), cu_q.cuda(), used_t.cuda(), bt.cuda(), max(Lq),
@@ -118,6 +123,16 @@ def test_paged(case, causal):
 def test_fp16_entry_points(d):
     _run_varlen(f"fp16_varlen_d{d}", (17, 200), (300, 200), 2, 1, d, True, 55 + d, dtype=torch.float16)
     _run_paged(f"fp16_paged_d{d}", (3, 64), (700, 64), 128, 2, 1, d, True, 56 + d, dtype=torch.float16)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_negative_scale(d, causal):
+    # scale -1/sqrt(d): scores of the opposite sign, packed and paged, without and with splits
+    sc = -float(d) ** -0.5
+    _run_varlen(f"neg_varlen_d{d}", (17, 200, 64), (300, 200, 64), 4, 2, d, causal, 57 + d, scale=sc)
+    _run_paged(f"neg_paged_d{d}", (3, 64), (700, 64), 128, 2, 1, d, causal, 58 + d, scale=sc)
+    _run_paged(f"neg_paged_split_d{d}", (1, 4), (900, 3000), 128, 2, 1, d, causal, 59 + d, scale=sc, splits=4)
 
 
 def test_paged_equals_varlen_on_the_same_keys():
