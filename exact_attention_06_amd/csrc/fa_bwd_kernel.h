@@ -182,7 +182,7 @@ bwd_dq_kernel(BwdParams p) {
 
   bwd_load_rows<D, NW, true>(kbase, kv_row, 0, Nk, k_lds0, wv, lane);
   bwd_load_rows<D, NW, true>(vbase, kv_row, 0, Nk, v_lds0, wv, lane);
-  __syncthreads();
+  tile_barrier();
   auto iteration = [&](const int j, auto par_tag) {
     constexpr int PAR = decltype(par_tag)::value;  // j & 1
     if (j + 1 < ntiles) {
@@ -252,7 +252,7 @@ bwd_dq_kernel(BwdParams p) {
         }
       }
     }
-    __syncthreads();
+    tile_barrier();
   };
   int j = 0;
   for (; j + 1 < ntiles; j += 2) {
@@ -364,7 +364,7 @@ bwd_dkdv_kernel(BwdParams p) {
   };
 
   if (total > 0) load_tile(0, 0);
-  __syncthreads();
+  tile_barrier();
   for (int n = 0; n < total; ++n) {
     const int buf = n & 1;
     if (n + 1 < total) load_tile(n + 1, buf ^ 1);
@@ -476,7 +476,7 @@ bwd_dkdv_kernel(BwdParams p) {
         }
       }
     }
-    __syncthreads();
+    tile_barrier();
   }
 
   if (k_lane < Nk) {

@@ -293,12 +293,12 @@ fwd_fp8_kernel(FwdParams p) {
       if constexpr (D == 128) asm volatile("" : "+v"(ones));
       gemm2(par ? v_lds1 : v_lds0, pb);
     }
-    __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
+    tile_barrier();  // the loads of this iteration have landed; LDS reads of it are done
   };
   using F = BoolC<false>;
   using U = BoolC<true>;
   load_kv(0, 0);
-  __syncthreads();
+  tile_barrier();
   int j = 0;
   for (; j + 1 < nfull; j += 2) {
     iteration(j, 0, F{});

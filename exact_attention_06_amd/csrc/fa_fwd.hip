@@ -170,32 +170,33 @@ size_t splitkv_ws_bytes(int B, int Nq, int Hq, int d, int splits) {
   return (size_t)splits * B * Hq * Nq * (size_t)(d + 1) * sizeof(float);
 }
 
-// Split count from measurements on MI355X (hd128 and hd256, 1..4 batches of 1k..8k tokens,
-// 8 or 16 heads): splitting pays while the plain grid has at most ~256 workgroups, more so
-// for causal shapes and long key ranges; beyond that the partials' workspace traffic costs
-// more than the extra parallelism brings. At least 4 key tiles per split.
+// Split count from a sweep on MI355X (plain grid against 1, 2, 3, 4, 6 and 8 splits; 1..4
+// batches of 1k..4k tokens, 8 or 16 heads, hd128 and hd256, causal and not, best of 3 x 40
+// launches): splitting pays only on a nearly empty GPU (at most 128 workgroups; 256 for long
+// causal hd256 ranges) with enough key tiles per split, because a split costs its partials'
+// fp32 traffic, the merge kernel and a workgroup's fixed work (prologue, first tile, stores).
+// One split through the split-KV path ran 15-35% slower than the plain grid at these sizes.
+// Rules, first match wins: {most workgroups, fewest key tiles, splits}.
+struct SplitRule {
+  int max_blocks, min_tiles, splits;
+};
+constexpr SplitRule kSplit128[] = {{64, 32, 4}, {128, 32, 2}};
+constexpr SplitRule kSplit128Causal[] = {{64, 32, 4}, {128, 64, 3}, {128, 32, 2}};
+constexpr SplitRule kSplit256[] = {{64, 24, 3}, {128, 48, 3}};
+constexpr SplitRule kSplit256Causal[] = {{64, 32, 4}, {128, 64, 2}, {256, 128, 3}};
+
 int num_splits(int B, int Nq, int Nk, int Hq, int d, int causal) {
   if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || (d != 128 && d != 256)) return 1;
   const int BR = d == 128 ? fa::Layout<128>::BR : fa::Layout<256>::BR;
   const int64_t blocks = (int64_t)B * Hq * ((Nq + BR - 1) / BR);
-  const int ntiles = (Nk + key_tile(d) - 1) / key_tile(d);
-  // Measured on MI355X (1-4 batches, 1k-8k tokens, 8 or 16 heads, 60 launches per point):
-  // non-causal splits pay only on a nearly empty GPU or over at least 2k keys (2 splits of
-  // 1k keys at 128 workgroups lost 7%); causal ones pay up to 512 workgroups when the key
-  // range is long (the diagonal work piles up on the last query tiles).
-  int s = 1;
-  if (blocks <= 64)
-    s = 4;
-  else if (blocks <= 160 && (causal || Nk >= 2048))
-    s = 2;
-  else if (blocks <= 256 && Nk >= 4096 && causal)
-    s = 3;
-  else if (blocks <= 512 && Nk >= 8192 && causal)
-    s = 2;
-  // a workgroup costs about six key tiles of fixed work (prologue, first and last tile,
-  // stores): non-causal chunks keep at least 16 tiles, causal ones (whose diagonal tiles pile
-  // up on the last query tiles) at least 4
-  return std::max(1, std::min(s, ntiles / (causal ? 4 : 16)));
+  const int64_t tiles = ((int64_t)Nk + key_tile(d) - 1) / key_tile(d);
+  auto pick = [&](const auto& rules) {
+    for (const SplitRule& r : rules)
+      if (blocks <= r.max_blocks && tiles >= r.min_tiles) return r.splits;
+    return 1;
+  };
+  if (d == 128) return causal ? pick(kSplit128Causal) : pick(kSplit128);
+  return causal ? pick(kSplit256Causal) : pick(kSplit256);
 }
 
 template <class T>

@@ -259,12 +259,12 @@ fwd_hd512_kernel(FwdParams p) {
       softmax(sc, pf, SPLIT ? pl : nullptr);
       gemm2(par ? v_lds1 : v_lds0, pf, SPLIT ? pl : nullptr);
     }
-    __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
+    tile_barrier();  // the loads of this iteration have landed; LDS reads of it are done
   };
   using F = BoolC<false>;
   using U = BoolC<true>;
   load_kv(0, 0);
-  __syncthreads();
+  tile_barrier();
   int j = 0;
   if (nfull > 0) {
     iteration(0, 0, U{}, F{});

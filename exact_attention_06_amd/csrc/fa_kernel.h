@@ -167,6 +167,15 @@ __device__ __forceinline__ X8 negate16(X8 x) {
   return __builtin_bit_cast(X8, u);
 }
 
+// Barrier that publishes K/V tiles loaded straight into LDS: each wave first waits for its own
+// buffer loads (vmcnt), then the workgroup meets. The compiler inserts that wait only where the
+// same wave reads the data afterwards (gfx950 barriers do not wait by themselves), while every
+// wave's share of a tile is read by all waves: only this order makes the whole tile visible.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 // Lane l and lane l^32 hold the same query row: the value of the other half.
 __device__ __forceinline__ float other_half(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
@@ -751,13 +760,13 @@ fwd_kernel(FwdParams p) {
       softmax(sc, pf, SPLIT ? pl : nullptr);
       gemm2(par, pf, SPLIT ? pl : nullptr);
     }
-    __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
+    tile_barrier();  // the loads of this iteration have landed; LDS reads of it are done
   };
   using F = BoolC<false>;
   using U = BoolC<true>;
   load_k(0, 0);
   load_v(0, 0);
-  __syncthreads();
+  tile_barrier();
   int j = 0;
   if (nfull > 0) {
     seq_iteration(0, 0, U{}, F{});
@@ -780,11 +789,11 @@ fwd_kernel(FwdParams p) {
   load_k(0, 0);
   load_v(0, 0);
   if (ntiles > 1) load_k(1, 1);
-  __syncthreads();  // waits for the loads (vmcnt) before the barrier
+  tile_barrier();  // waits for the loads (vmcnt) before the barrier
 
   f32x16 s_a[MT1], s_b[MT1];
   gemm1(0, s_a);
-  __syncthreads();  // every wave has read K(0) before iteration 0 reloads its buffer
+  tile_barrier();  // every wave has read K(0) before iteration 0 reloads its buffer
 
   // ---- tile loop. Iteration j: loads of K(j+2), V(j+1) in flight; softmax(j) with the
   //      MFMAs of GEMM1(j+1); GEMM2(j); barrier. Scores of tile j are in `sc`, those of
@@ -820,7 +829,7 @@ fwd_kernel(FwdParams p) {
       gemm2(par, pf, SPLIT ? pl : nullptr);
       if (next_active) mt_cur = rowmax(sn);
     }
-    __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
+    tile_barrier();  // the loads of this iteration have landed; LDS reads of it are done
   };
 
   // Main iteration (unmasked tile j, tile j+1 exists), with an explicit instruction order:
@@ -915,7 +924,7 @@ fwd_kernel(FwdParams p) {
     lL += sumL0 + sumL1;
     mx = __builtin_fmaxf(mx, other_half(mx));
     mt_cur = mx * c;
-    __syncthreads();  // the loads of this iteration have landed; LDS reads of it are done
+    tile_barrier();  // the loads of this iteration have landed; LDS reads of it are done
   };
 
   using T0 = BoolC<false>;

@@ -306,3 +306,27 @@ def test_splitkv_fp16():
     torch.cuda.synchronize()
     O_ref, L_ref = attention_ref(q, k, v, True, 1.0 / 16)
     _compare("splitkv_fp16", o, lse, O_ref, L_ref)
+
+
+# ---------------------------------------------------------------- repeated launches
+
+@pytest.mark.parametrize("wname", ["hd128_N8192_mha", "hd256_N8192", "hd512_N8192", "video"])
+def test_repeated_full_size_launches_are_bitwise_equal(wname):
+    # Every wave loads a share of each K/V tile into LDS and every wave reads all of it, so a
+    # tile barrier must wait for the wave's own loads first; a missing wait shows up as
+    # launch-to-launch differences at full size (seen on the video shape before the fix).
+    w = W.by_name(wname)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    q = torch.randn((w.B, w.N, w.Hq, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((w.B, w.N, w.Hkv, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((w.B, w.N, w.Hkv, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    if w.k_spike:
+        k[:, 0::16] *= 4
+    for causal in w.causal_modes:
+        _say(f"[gpu] repeated launches {wname} causal={causal}")
+        o0, l0 = fa.forward(q, k, v, causal=causal, scale=w.scale)
+        for _ in range(3):
+            o1, l1 = fa.forward(q, k, v, causal=causal, scale=w.scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o0, o1) and torch.equal(l0, l1), f"{wname} causal={causal}"

@@ -139,3 +139,21 @@ RB = [_random_case(i) for i in range(12)]
 def test_bwd_random_shape(case):
     name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype = case
     _run(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=dtype)
+
+
+@pytest.mark.parametrize("wname", ["hd128_N8192_mha", "hd256_N8192"])
+def test_bwd_repeated_full_size_launches_are_bitwise_equal(wname):
+    # the backward kernels stream Q/dO and K/V tiles loaded by all waves: launches must agree
+    w = W.by_name(wname)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    q, k, v, do = (torch.randn((w.B, w.N, h, w.d), generator=g, device="cuda").to(torch.bfloat16)
+                   for h in (w.Hq, w.Hkv, w.Hkv, w.Hq))
+    for causal in (False, True):
+        _say(f"[gpu] bwd repeated launches {wname} causal={causal}")
+        o, lse = fa.forward(q, k, v, causal=causal, scale=w.scale)
+        r0 = fa.backward(q, k, v, o, lse, do, causal=causal, scale=w.scale)
+        r1 = fa.backward(q, k, v, o, lse, do, causal=causal, scale=w.scale)
+        torch.cuda.synchronize()
+        for a, b in zip(r0, r1):
+            assert torch.equal(a, b)

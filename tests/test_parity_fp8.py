@@ -154,3 +154,19 @@ def test_fp8_scales_enter_exactly():
     o2, l2 = fa.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), qs, ks, 2 * vs)
     torch.cuda.synchronize()
     assert torch.equal(o2, 2 * o1) and torch.equal(l1, l2)
+
+
+def test_fp8_repeated_full_size_launches_are_bitwise_equal():
+    # every wave reads every wave's share of each K/V tile: launches must agree bit for bit
+    w = W.by_name("hd256_N8192")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    x = [torch.randn((w.B, w.N, h, w.d), generator=g, device="cuda") for h in (w.Hq, w.Hkv, w.Hkv)]
+    (q8, qs), (k8, ks), (v8, vs) = (_quant(t) for t in x)
+    for causal in (False, True):
+        _say(f"[gpu] fp8 repeated launches causal={causal}")
+        o0, l0 = fa.forward_fp8(q8, k8, v8, qs, ks, vs, causal=causal, scale=w.scale)
+        for _ in range(2):
+            o1, l1 = fa.forward_fp8(q8, k8, v8, qs, ks, vs, causal=causal, scale=w.scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o0, o1) and torch.equal(l0, l1)
