@@ -180,8 +180,11 @@ def _check_tensor(name, t, torch):
         raise ValueError(f"{name} must be contiguous")
 
 
-def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None):
-    """Gradients (dq, dk, dv) of sum(o * dout) for o, lse = forward(q, k, v, causal, scale)."""
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, noalloc: bool = False):
+    """Gradients (dq, dk, dv) of sum(o * dout) for o, lse = forward(q, k, v, causal, scale).
+
+    noalloc=True calls fa_bwd_noalloc (bf16 only): no workspace, D kept in the library's
+    fixed device scratch (calls that overlap on one GPU race on it)."""
     import torch
 
     lib = _lib.load()
@@ -210,6 +213,17 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
+    if noalloc:
+        if q.dtype != torch.bfloat16:
+            raise ValueError("the allocation-free backward pass takes bfloat16 tensors")
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+            rc = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Nq, Nk, Hq, Hkv,
+                                    d, int(bool(causal)), float(scale), stream)
+        if rc != 0:
+            _raise(rc)
+        return dq, dk, dv
     nbytes = int(lib.fa_bwd_workspace_bytes(B, Nq, Hq))
     ws = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):

@@ -25,6 +25,8 @@ FA_ERR_TOO_LARGE = -7
 FA_ERR_LAUNCH = -8
 FA_ERR_WORKSPACE = -9
 FA_ERR_PAGE = -10
+FA_ERR_SCRATCH = -11
+FA_BWD_NOALLOC_MAX_ROWS = 8 << 20  # include/fa_fwd.h
 
 _lib = None
 
@@ -97,6 +99,10 @@ def load():
             fn = getattr(lib, name)
             fn.argtypes = _BWD_ARGS
             fn.restype = _I
+        # q, k, v, o, lse, dout, dq, dk, dv, B, Nq, Nk, Hq, Hkv, d, causal, scale, stream
+        lib.fa_bwd_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                       ctypes.c_float, _P]
+        lib.fa_bwd_noalloc.restype = _I
         lib.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I]
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_check.argtypes = _CHECK_ARGS

@@ -5,6 +5,7 @@
 
 #include <climits>
 #include <algorithm>
+#include <mutex>
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
@@ -15,7 +16,31 @@
 #include "fa_fp8_kernel.h"
 #include "fa_hd512_kernel.h"
 
+// Device scratch of the allocation-free backward entry point: D = rowsum(dO * O) for up to
+// FA_BWD_NOALLOC_MAX_ROWS rows. In host code this name is only a handle for the runtime; the
+// device address of each GPU's copy comes from hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) float scratch[FA_BWD_NOALLOC_MAX_ROWS];
+
 namespace {
+
+// Per-device address of `scratch`, resolved once per device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// 0 and the address of the current device's scratch, or FA_ERR_LAUNCH.
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return FA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
 
 template <int D, bool CAUSAL, class T, int VM>
 int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
@@ -349,18 +374,27 @@ int launch_bwd(const fa::BwdParams& base, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-template <class T>
-int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-            void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, int B, int Nq, int Nk, int Hq, int Hkv,
-            int d, int causal, float scale, void* stream) {
+// every host check of the backward pass except the workspace
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              const void* dq, const void* dk, const void* dv, int B, int Nq, int Nk, int Hq, int Hkv, int d,
+              int causal, float scale) {
   int st = check(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale);
   if (st != FA_OK) return st;
   if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (((uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15) return FA_ERR_ALIGN;
-  if (!ws || ws_bytes < bwd_ws_bytes(B, Nq, Hq) || ((uintptr_t)ws & 3)) return FA_ERR_WORKSPACE;
   const int64_t BR = fa::BwdCfg<128>::NW * 32;
   if ((int64_t)B * Hq * ((Nq + BR - 1) / BR) > INT_MAX || (int64_t)B * Hkv * ((Nk + BR - 1) / BR) > INT_MAX)
     return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+template <class T>
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+            void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, int B, int Nq, int Nk, int Hq, int Hkv,
+            int d, int causal, float scale, void* stream) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Nq, Nk, Hq, Hkv, d, causal, scale);
+  if (st != FA_OK) return st;
+  if (!ws || ws_bytes < bwd_ws_bytes(B, Nq, Hq) || ((uintptr_t)ws & 3)) return FA_ERR_WORKSPACE;
   fa::BwdParams prm;
   prm.q = (const uint8_t*)q;
   prm.k = (const uint8_t*)k;
@@ -532,6 +566,21 @@ int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const
                           causal, scale, stream);
 }
 
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal,
+                   float scale, void* stream) {
+  // every host check of fa_bwd, then the scratch limit, then the device address: no HIP call
+  // before the arguments are known good
+  int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Nq, Nk, Hq, Hkv, d, causal, scale);
+  if (st != FA_OK) return st;
+  if ((int64_t)B * Hq * Nq > (int64_t)FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != FA_OK) return st;
+  return run_bwd<fa::Bf16>(q, k, v, o, lse, dout, dq, dk, dv, ws, sizeof(scratch), B, Nq, Nk, Hq, Hkv, d, causal,
+                           scale, stream);
+}
+
 const char* fa_strerror(int code) {
   switch (code) {
     case FA_OK: return "ok";
@@ -545,6 +594,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than the *_workspace_bytes size";
     case FA_ERR_PAGE: return "paged K/V: page_size must be a positive multiple of 64, num_pages and max_pages positive";
+    case FA_ERR_SCRATCH: return "fa_bwd_noalloc: B * Hq * Nq exceeds the fixed device scratch (FA_BWD_NOALLOC_MAX_ROWS rows)";
     default: return "unknown fa status code";
   }
 }

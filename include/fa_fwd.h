@@ -60,9 +60,11 @@ enum fa_status {
   FA_ERR_LAUNCH = -8,       /* the HIP launch reported an error                            */
   FA_ERR_WORKSPACE = -9,    /* workspace NULL, not 16-byte aligned (split-KV) or smaller
                                than fa_bwd_workspace_bytes / fa_fwd_splitkv_workspace_bytes */
-  FA_ERR_PAGE = -10         /* paged K/V: page_size not a positive multiple of 64, or
+  FA_ERR_PAGE = -10,        /* paged K/V: page_size not a positive multiple of 64, or
                                num_pages / max_pages not positive, or a page extent
                                (pages x page_size) above 2^31 - 1                          */
+  FA_ERR_SCRATCH = -11      /* fa_bwd_noalloc: the problem needs more than the library's
+                               fixed device scratch (FA_BWD_NOALLOC_MAX_ROWS rows)          */
 };
 
 /* Forward pass, bf16 q/k/v/o, fp32 LSE. Arguments as described above; `scale` multiplies
@@ -274,6 +276,25 @@ int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const
                const void* dout, void* dq, void* dk, void* dv, void* workspace,
                size_t workspace_bytes, int B, int Nq, int Nk, int Hq, int Hkv, int d,
                int causal, float scale, void* stream);
+
+/*
+ * Allocation-free backward pass, for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): fa_bwd's operation, layouts and kernels (bf16), with D kept in a device array
+ * of the library itself (32 MiB per GPU, FA_BWD_NOALLOC_MAX_ROWS fp32 rows, allocated when
+ * the library's code object is loaded on that GPU and held until the process ends). The
+ * call allocates nothing. The first call on a GPU resolves that GPU's copy of the array
+ * once (hipGetSymbolAddress, with the GPU current); a failure there returns FA_ERR_LAUNCH.
+ * Limit: B * Hq * Nq <= FA_BWD_NOALLOC_MAX_ROWS, else FA_ERR_SCRATCH (checked on the host
+ * before any HIP call). All calls on one GPU share its array: calls that overlap in time on
+ * one GPU (different streams, or threads) race on it and give wrong gradients; serialise
+ * them. Nothing needs clearing between calls (every launch writes all of D before reading it).
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS (8u << 20)
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq,
+                   int Hkv, int d, int causal, float scale, void* stream);
 
 #ifdef __cplusplus
 }

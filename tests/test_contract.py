@@ -39,7 +39,7 @@ def test_library_exports_every_header_symbol():
                           "fa_fwd_splitkv_workspace_bytes", "fa_fwd_num_splits", "fa_fwd_fp8",
                           "fa_fwd_var_splitkv_workspace_bytes", "fa_fwd_varlen_splitkv",
                           "fa_fwd_varlen_splitkv_f16", "fa_fwd_paged_splitkv", "fa_fwd_paged_splitkv_f16",
-                          "fa_fwd_var_num_splits"}
+                          "fa_fwd_var_num_splits", "fa_bwd_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -122,11 +122,11 @@ def test_entry_points_reject_before_any_hip_call(entry):
 
 def test_strerror_covers_codes():
     seen = set()
-    for code in range(-10, 1):
+    for code in range(-11, 1):
         msg = _lib.strerror(code)
         assert msg and msg != "unknown fa status code"
         seen.add(msg)
-    assert len(seen) == 11
+    assert len(seen) == 12
     assert _lib.strerror(-99) == "unknown fa status code"
 
 
@@ -168,6 +168,32 @@ def test_bwd_rejects_before_any_hip_call(entry):
     assert _bwd(fn, ws=0) == _lib.FA_ERR_WORKSPACE
     assert _bwd(fn, wsb=4 * 2 * 300 * 8 - 4) == _lib.FA_ERR_WORKSPACE
     assert _bwd(fn, ws=A + 0x802) == _lib.FA_ERR_WORKSPACE
+
+
+def _bwd_noalloc(**kw):
+    a = dict(GOOD, **kw)
+    return _lib.load().fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a.get("do", A + 0x500),
+                                      a.get("dq", A + 0x600), a.get("dk", A + 0x700), a.get("dv", A + 0x780),
+                                      a["B"], a["Nq"], a["Nk"], a["Hq"], a["Hkv"], a["d"], a["causal"],
+                                      ctypes.c_float(a["scale"]), None)
+
+
+def test_bwd_noalloc_rejects_before_any_hip_call():
+    # the allocation-free backward pass checks as fa_bwd does, then its fixed scratch limit
+    assert _bwd_noalloc(q=0) == _lib.FA_ERR_NULL
+    assert _bwd_noalloc(do=0) == _lib.FA_ERR_NULL
+    assert _bwd_noalloc(dv=0) == _lib.FA_ERR_NULL
+    assert _bwd_noalloc(d=96) == _lib.FA_ERR_HEADDIM
+    assert _bwd_noalloc(d=512) == _lib.FA_ERR_HEADDIM
+    assert _bwd_noalloc(causal=1, Nk=17) == _lib.FA_ERR_CAUSAL_SHAPE
+    assert _bwd_noalloc(Hkv=3) == _lib.FA_ERR_SHAPE
+    assert _bwd_noalloc(scale=math.nan) == _lib.FA_ERR_SCALE
+    assert _bwd_noalloc(dq=A + 0x604) == _lib.FA_ERR_ALIGN
+    assert _bwd_noalloc(do=A + 0x508) == _lib.FA_ERR_ALIGN
+    rows = _lib.FA_BWD_NOALLOC_MAX_ROWS
+    assert _bwd_noalloc(B=1, Hq=16, Hkv=16, Nq=rows // 16 + 1, Nk=4096) == _lib.FA_ERR_SCRATCH
+    assert _bwd_noalloc(B=2, Hq=8, Hkv=8, Nq=rows // 16 + 1, Nk=rows // 16 + 1, causal=1) == _lib.FA_ERR_SCRATCH
+    assert "scratch" in _lib.strerror(_lib.FA_ERR_SCRATCH)
 
 
 # ---- variable-length and paged entry points: every rejection happens on the host
