@@ -42,11 +42,11 @@ int noalloc_scratch(void** out) {
   return FA_OK;
 }
 
-template <int D, bool CAUSAL, class T, int VM>
+template <int D, bool CAUSAL, class T, int VM, int WV = fa::TileCfg<D>::NW>
 int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
-  using L = fa::Layout<D>;
+  using L = fa::Layout<D, WV>;
   // the kernel's K/V buffers are static LDS (L::LDS bytes, within gfx950's 160 KB per CU)
-  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, T, VM>), dim3(grid), dim3(L::NW * 64), 0, stream, prm);
+  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, T, VM, WV>), dim3(grid), dim3(L::NW * 64), 0, stream, prm);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   if (VM == 2) {  // split-KV: merge the partials
     const size_t threads = (size_t)prm.B * prm.Hq * prm.Nq * (D / 8);
@@ -74,11 +74,31 @@ void set_scale(P& prm, float scale) {
   prm.c = prm.zero_scores ? fa::LOG2E : a;
 }
 
+// hd128 takes the 4-wave workgroup when the 8-wave grid (without splits; for
+// variable-length batches the grid sized by the longest query sequence) has at most this many
+// workgroups, one per CU (measured on MI355X: +14-30% on causal shapes with 64-256
+// workgroups, 1-4% slower on full grids). Every form decides alike, so that one sequence
+// through the variable-length path and the dense path, or one split and none, take the same
+// kernel configuration and agree bit for bit.
+constexpr int kSmallGrid128 = 256;
+
+bool use_4wave(int B, int Nq, int Hq, int d) {
+  const int64_t BR8 = fa::Layout<128>::BR;
+  return d == 128 && (int64_t)B * Hq * ((Nq + BR8 - 1) / BR8) <= kSmallGrid128;
+}
+
 template <int VM, class T>
 int dispatch(fa::FwdParams& prm, int d, int causal, hipStream_t s) {
+  const int splits = VM >= 2 ? prm.splits : 1;
+  if (d == 128 && use_4wave(prm.B, prm.Nq, prm.Hq, d)) {
+    constexpr int BR = fa::Layout<128, 4>::BR;
+    prm.nqt = (prm.Nq + BR - 1) / BR;
+    const int grid = prm.B * prm.Hq * prm.nqt * splits;
+    return causal ? launch<128, true, T, VM, 4>(prm, grid, s) : launch<128, false, T, VM, 4>(prm, grid, s);
+  }
   const int BR = d == 128 ? fa::Layout<128>::BR : fa::Layout<256>::BR;
   prm.nqt = (prm.Nq + BR - 1) / BR;
-  const int grid = prm.B * prm.Hq * prm.nqt * (VM >= 2 ? prm.splits : 1);
+  const int grid = prm.B * prm.Hq * prm.nqt * splits;
   if (d == 128)
     return causal ? launch<128, true, T, VM>(prm, grid, s) : launch<128, false, T, VM>(prm, grid, s);
   return causal ? launch<256, true, T, VM>(prm, grid, s) : launch<256, false, T, VM>(prm, grid, s);
@@ -201,12 +221,15 @@ size_t splitkv_ws_bytes(int B, int Nq, int Hq, int d, int splits) {
 // causal hd256 ranges) with enough key tiles per split, because a split costs its partials'
 // fp32 traffic, the merge kernel and a workgroup's fixed work (prologue, first tile, stores).
 // One split through the split-KV path ran 15-35% slower than the plain grid at these sizes.
-// Rules, first match wins: {most workgroups, fewest key tiles, splits}.
+// Rules, first match wins: {most workgroups of the 8-wave (hd128) or 4-wave (hd256) grid,
+// fewest key tiles, splits}.
 struct SplitRule {
   int max_blocks, min_tiles, splits;
 };
-constexpr SplitRule kSplit128[] = {{64, 32, 4}, {128, 32, 2}};
-constexpr SplitRule kSplit128Causal[] = {{64, 32, 4}, {128, 64, 3}, {128, 32, 2}};
+// (hd128 measured with its 4-wave form on these small grids, which already doubles the
+// workgroups: non-causal splits no longer pay there)
+constexpr SplitRule kSplit128[] = {{-1, 0, 1}};
+constexpr SplitRule kSplit128Causal[] = {{64, 32, 2}, {128, 64, 3}};
 constexpr SplitRule kSplit256[] = {{64, 24, 3}, {128, 48, 3}};
 constexpr SplitRule kSplit256Causal[] = {{64, 32, 4}, {128, 64, 2}, {256, 128, 3}};
 

@@ -284,9 +284,13 @@ enum LoopMode { PIPE = 0, SEQ = 1 };
 template <> struct TileCfg<128> { static constexpr int NW = 8, BC = 64, WPE = 2, MODE = PIPE; };
 template <> struct TileCfg<256> { static constexpr int NW = 4, BC = 32, WPE = 2, MODE = SEQ; };
 
-template <int D>
+// WV: waves per workgroup. hd128 has two forms: 8 waves (256 query rows, one workgroup per
+// CU) and 4 waves (128 rows, two workgroups per CU) for grids that do not fill the GPU twice
+// over, where twice the workgroups and one workgroup's prologue hidden under the other's
+// tiles outweigh the second K/V stream per CU.
+template <int D, int WV = TileCfg<D>::NW>
 struct Layout {
-  static constexpr int NW = TileCfg<D>::NW, BC = TileCfg<D>::BC;
+  static constexpr int NW = WV, BC = TileCfg<D>::BC;
   static constexpr int BR = NW * 32;           // query rows per workgroup
   static constexpr int KROW = D * 2 + 16;      // padded LDS row pitch of K (bytes)
   static constexpr int VROW = D * 2 + 64;      // padded LDS row pitch of V (bytes)
@@ -295,10 +299,11 @@ struct Layout {
   // A tile is written by 64-slot (1 KB) direct-to-LDS loads spread evenly over the NL
   // loading waves, waves LB .. LB + NL - 1; each buffer is rounded up so that every loading
   // wave issues the same number of whole loads (the slots past the tile receive zeros).
-  // hd128: the four younger waves load (5 loads each per tile and buffers of 20 KB, against
-  // 3 per wave for all eight and 24 KB buffers); they are the ones that lag at the tile
-  // barriers, and the loads at the top of an iteration let the older waves run on.
-  static constexpr int NL = D == 128 ? NW / 2 : NW;
+  // hd128 with 8 waves: the four younger waves load (5 loads each per tile and buffers of
+  // 20 KB, against 3 per wave for all eight and 24 KB buffers); they are the ones that lag at
+  // the tile barriers, and the loads at the top of an iteration let the older waves run on.
+  // With 4 waves all of them load (two loading waves were 20-40% slower on causal shapes).
+  static constexpr int NL = D == 128 && NW == 8 ? NW / 2 : NW;
   static constexpr int LB = NW - NL;
   static constexpr int KPW = (KT / 16 + 64 * NL - 1) / (64 * NL);  // K loads per loading wave
   static constexpr int VPW = (VT / 16 + 64 * NL - 1) / (64 * NL);  // V loads per loading wave
@@ -309,13 +314,13 @@ struct Layout {
 // VM: 0 dense batch, 1 variable-length batch (packed or paged K/V), 2 dense batch with the
 // key range of each query tile split over several blocks (split-KV), 3 variable-length batch
 // with split-KV (every sequence's key tiles cut into chunks of tps tiles).
-template <int D, bool CAUSAL, class T, int VM>
-__global__ void __launch_bounds__(TileCfg<D>::NW * 64, TileCfg<D>::WPE)
+template <int D, bool CAUSAL, class T, int VM, int WV = TileCfg<D>::NW>
+__global__ void __launch_bounds__(WV * 64, TileCfg<D>::WPE)
 fwd_kernel(FwdParams p) {
   constexpr bool VAR = VM == 1 || VM == 3, SPLITK = VM == 2 || VM == 3;
   using x8 = typename T::x8;
   using x2 = typename T::x2;
-  using L = Layout<D>;
+  using L = Layout<D, WV>;
   constexpr int NW = L::NW, BC = L::BC, BR = L::BR;
   constexpr int NT = NW * 64;
   constexpr int KS1 = D / 16;       // GEMM1 k-steps (over head dim)
