@@ -14,7 +14,6 @@ query rows of the same workload (a reported baseline, not the target).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -41,13 +40,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    cdir = os.path.join(ROOT, "exact_attention_06_amd", "csrc")
-    for n in sorted(os.listdir(cdir)):
-        with open(os.path.join(cdir, n), "rb") as f:
-            h.update(n.encode() + f.read())
-    return h.hexdigest()[:16]
+from exact_attention_06_amd.profile_summary import kernel_source_hash  # noqa: E402
 
 
 def gpu_inputs(w, torch):

@@ -41,11 +41,11 @@ struct BwdParams {
   int B, Nq, Nk, Hq, Hkv;
   int group;
   int ntile;    // work tiles per (b, head) of the kernel (query tiles or key tiles)
-  float c;      // |scale| * log2(e); log2(e) when zero_scores is set
+  float c;      // scale * log2(e), of either sign (P = exp2(c s - LSE log2(e)) needs no
+                // running maximum; masked entries are set to 0 after the exp); log2(e) when
+                // zero_scores is set
   float scale;  // the signed scale (dQ = scale dS K, dK = scale dS^T Q)
   int zero_scores;  // scale is zero (or below the normal range): every score is exactly 0
-  int neg_scores;   // scale < 0: the operand held in registers for S (Q in the dq kernel,
-                    // K in the dk/dv kernel) enters with its sign flipped, so c stays positive
 };
 
 template <int D>
@@ -158,10 +158,6 @@ bwd_dq_kernel(BwdParams p) {
   if (p.zero_scores) {  // zero scale: S = 0 exactly (masked scores stay -inf)
 #pragma unroll
     for (int t = 0; t < KS1; ++t) qf[t] = x8{};
-  }
-  if (p.neg_scores) {  // negative scale: S = |scale| (-Q) K^T, exact
-#pragma unroll
-    for (int t = 0; t < KS1; ++t) qf[t] = negate16(qf[t]);
   }
   const float dsum = dpart + other_half(dpart);
   const size_t lrow = ((size_t)b * p.Hq + hq) * Nq + q_ld;
@@ -321,10 +317,6 @@ bwd_dkdv_kernel(BwdParams p) {
   if (p.zero_scores) {  // zero scale: S = 0 exactly (masked scores stay -inf)
 #pragma unroll
     for (int t = 0; t < KS1; ++t) kf[t] = x8{};
-  }
-  if (p.neg_scores) {  // negative scale: S = |scale| Q (-K)^T, exact
-#pragma unroll
-    for (int t = 0; t < KS1; ++t) kf[t] = negate16(kf[t]);
   }
   const float c = p.c;
   f32x16 dk[MT2], dv[MT2];

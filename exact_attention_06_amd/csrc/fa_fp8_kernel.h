@@ -84,6 +84,7 @@ fwd_fp8_kernel(FwdParams p) {
 
   // Q (B operand of GEMM1): lane holds query q_ld, head-dim values 64t + 32hh .. +31
   i32x8 qf[KS1];
+  const int sgn8 = p.neg_scores ? (int)0x80808080u : 0;
   {
     const uint8_t* qp = p.q + (((size_t)b * Nq + q_ld) * p.Hq + hq) * (size_t)D;
 #pragma unroll
@@ -94,8 +95,8 @@ fwd_fp8_kernel(FwdParams p) {
         qf[t][e] = (int)lo[e];
         qf[t][4 + e] = (int)hi[e];
       }
-      if (p.neg_scores)  // negative scale: -Q (e4m3 sign bit 7 of every byte, exact)
-        for (int e = 0; e < 8; ++e) qf[t][e] ^= (int)0x80808080u;
+      // negative scale: -Q (e4m3 sign bit 7 of every byte, exact), as an unconditional xor
+      for (int e = 0; e < 8; ++e) qf[t][e] ^= sgn8;
       if (p.zero_scores) qf[t] = i32x8{};
     }
   }

@@ -436,7 +436,9 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   prm.Hkv = Hkv;
   prm.group = Hq / Hkv;
   prm.ntile = 0;
-  set_scale(prm, scale);  // as in the forward pass
+  // zero (or subnormal) scale as in the forward pass; otherwise the signed c
+  prm.zero_scores = !(std::fabs(scale) * fa::LOG2E >= FLT_MIN);
+  prm.c = prm.zero_scores ? fa::LOG2E : scale * fa::LOG2E;
   prm.scale = scale;
   hipStream_t s = (hipStream_t)stream;
   if (d == 128)

@@ -83,10 +83,10 @@ fwd_hd512_kernel(FwdParams p) {
 #pragma unroll
       for (int t = 0; t < KS1; ++t) qf[t] = x8{};
     }
-    if (p.neg_scores) {  // negative scale: -Q (exact) with c = |scale| * log2(e)
+    // negative scale: -Q (exact) with c = |scale| * log2(e)
+    const unsigned sgn = p.neg_scores ? 0x80008000u : 0u;
 #pragma unroll
-      for (int t = 0; t < KS1; ++t) qf[t] = negate16(qf[t]);
-    }
+    for (int t = 0; t < KS1; ++t) qf[t] = sign16(qf[t], sgn);
   }
 
   f32x16 acc[MT2];

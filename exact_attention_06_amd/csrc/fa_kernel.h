@@ -157,13 +157,15 @@ struct FwdParams {
 template <bool V> struct BoolC { static constexpr bool value = V; };
 template <int V> struct IntC { static constexpr int value = V; };
 
-// Sign flip of every 16-bit element of a fragment (bf16 / fp16: bit 15). Exact, so that
-// |scale| * (-q) . k equals scale * q . k bit for bit and c = |scale| * log2(e) stays >= 0,
-// which the row maximum relies on (max(s) * c == max(s * c)).
+// Sign of every 16-bit element of a fragment (bf16 / fp16: bit 15) flipped where `mask` has
+// it set: mask = 0x80008000 for a negative scale, else 0. Exact, so that |scale| * (-q) . k
+// equals scale * q . k bit for bit and c = |scale| * log2(e) stays >= 0, which the row maximum
+// relies on (max(s) * c == max(s * c)). An unconditional xor with a uniform mask: a
+// conditional flip made the compiler spill Q fragments and reload them inside the tile loop.
 template <class X8>
-__device__ __forceinline__ X8 negate16(X8 x) {
+__device__ __forceinline__ X8 sign16(X8 x, unsigned mask) {
   u32x4 u = __builtin_bit_cast(u32x4, x);
-  u ^= 0x80008000u;
+  u ^= mask;
   return __builtin_bit_cast(X8, u);
 }
 
@@ -478,10 +480,9 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int t = 0; t < KS1; ++t) qf[t] = x8{};
     }
-    if (p.neg_scores) {
+    const unsigned sgn = p.neg_scores ? 0x80008000u : 0u;
 #pragma unroll
-      for (int t = 0; t < KS1; ++t) qf[t] = negate16(qf[t]);
-    }
+    for (int t = 0; t < KS1; ++t) qf[t] = sign16(qf[t], sgn);
   }
 
   f32x16 acc[MT2];

@@ -11,6 +11,7 @@ into a markdown table:
 
 import json
 import os
+import re
 import sys
 
 O_MAX = 1e-2
@@ -24,28 +25,78 @@ def record(**entry):
         f.write(json.dumps(entry) + "\n")
 
 
+# the workloads the benchmark and the pages' configurations name (tiny, ragged, the hd128 /
+# hd256 / hd512 sweeps, the spiked-key video shape): listed case by case
+NAMED = re.compile(r"^(tiny|ragged|hd128_N\d+_(mha|gqa4)|hd256_N\d+|hd512_N\d+|video)(/|$)")
+
+
+def _line(r):
+    flag = r["o_max"] > O_MAX and r["o_max_small"] <= O_MAX
+    ex = f"{r['ex_big']:.2e}" if r["n_big"] else "-"
+    return (f"| {r['case']} | {r['o_max']:.2e} | {r['o_max_small']:.2e} | {r['o_mean']:.2e} | {r['lse_max']:.2e} "
+            f"| {r['n_big']} | {ex} | {'yes' if flag else 'no'} |")
+
+
+HEADER = """# Parity record: every bf16/fp16 forward comparison of the GPU suite
+
+One GPU run of the whole suite on the current kernel sources, each case against the fp64 oracle (all rows, or the
+seeded sampled rows of the full-size workloads). Commands (from the repository root):
+
+    FA_PARITY_RECORD=gpurun_out/parity.jsonl python -u -m pytest tests -m gpu -x -v -s
+    python3 tests/parity_record.py gpurun_out/parity.jsonl > profiles/parity_record.md
+
+The bar: O max-abs <= 1e-2 and mean-abs <= 1e-3, LSE max-abs <= 1e-3. Where |O_ref| >= 4 the bf16 grid spacing is
+2^-5, so the correctly rounded value itself can be 1.56e-2 away; such elements are held to half a bf16 ulp plus
+1e-2 - 2^-7, and the tables give their count and worst excess over the half ulp. A case that two tests check with
+the same figures is listed once.
+"""
+
+
 def main(path):
-    rows = [json.loads(line) for line in open(path) if line.strip()]
-    print("| case | O max-abs | O max-abs, \\|O_ref\\| < 4 | O mean-abs | LSE max-abs | elements with \\|O_ref\\| >= 4 "
-          "| their worst excess over half a bf16 ulp | over 1e-2 only on \\|O_ref\\| >= 4 |")
-    print("|---|---|---|---|---|---|---|---|")
-    only_big = []
-    for r in rows:
-        flag = r["o_max"] > O_MAX and r["o_max_small"] <= O_MAX
-        if flag:
-            only_big.append(r["case"])
-        ex = f"{r['ex_big']:.2e}" if r["n_big"] else "-"
-        print(f"| {r['case']} | {r['o_max']:.2e} | {r['o_max_small']:.2e} | {r['o_mean']:.2e} | {r['lse_max']:.2e} "
-              f"| {r['n_big']} | {ex} | {'yes' if flag else 'no'} |")
+    rows, seen = [], set()
+    for line in open(path):
+        if line.strip() and line.strip() not in seen:
+            seen.add(line.strip())
+            rows.append(json.loads(line))
+    print(HEADER)
+    named = [r for r in rows if NAMED.match(r["case"])]
+    other = [r for r in rows if not NAMED.match(r["case"])]
+    head = ("| case | O max-abs | O max-abs, \\|O_ref\\| < 4 | O mean-abs | LSE max-abs | elements with \\|O_ref\\| >= 4 "
+            "| their worst excess over half a bf16 ulp | over 1e-2 only on \\|O_ref\\| >= 4 |")
+    print("## Named workloads (configurations and sweeps)")
     print()
-    worst = max(rows, key=lambda r: r["o_max"]) if rows else None
-    print(f"{len(rows)} cases. Largest O max-abs: {worst['o_max']:.3e} ({worst['case']}). "
-          f"Largest LSE max-abs: {max(r['lse_max'] for r in rows):.3e}. Largest O mean-abs: "
-          f"{max(r['o_mean'] for r in rows):.3e}.")
+    print(head)
+    print("|---|---|---|---|---|---|---|---|")
+    for r in named:
+        print(_line(r))
+    print()
+    print("## Every other case (small, ragged, rectangular, GQA, zero / negative / large scales, split-KV, random")
+    print("shapes, variable-length and paged), summarised")
+    print()
+    if other:
+        print(f"{len(other)} cases: largest O max-abs {max(r['o_max'] for r in other):.3e}, largest O max-abs on "
+              f"|O_ref| < 4 {max(r['o_max_small'] for r in other):.3e}, largest O mean-abs "
+              f"{max(r['o_mean'] for r in other):.3e}, largest LSE max-abs {max(r['lse_max'] for r in other):.3e}, "
+              f"{sum(r['n_big'] for r in other)} elements with |O_ref| >= 4.")
+        big = [r for r in other if r["o_max"] > O_MAX]
+        if big:
+            print()
+            print("Cases above 1e-2 (on |O_ref| >= 4 elements only where the last column says so):")
+            print()
+            print(head)
+            print("|---|---|---|---|---|---|---|---|")
+            for r in big:
+                print(_line(r))
+    print()
+    only_big = [r["case"] for r in rows if r["o_max"] > O_MAX and r["o_max_small"] <= O_MAX]
+    worst = max(rows, key=lambda r: r["o_max"])
+    print(f"All {len(rows)} cases: largest O max-abs {worst['o_max']:.3e} ({worst['case']}), largest LSE max-abs "
+          f"{max(r['lse_max'] for r in rows):.3e}, largest O mean-abs {max(r['o_mean'] for r in rows):.3e}; "
+          f"largest O max-abs on |O_ref| < 4 {max(r['o_max_small'] for r in rows):.3e}.")
     if only_big:
-        print(f"Cases above 1e-2 only on elements with |O_ref| >= 4: {', '.join(only_big)}.")
+        print(f"Above 1e-2 only on elements with |O_ref| >= 4: {', '.join(sorted(set(only_big)))}.")
     else:
-        print("No case exceeds 1e-2 on any element, including those with |O_ref| >= 4.")
+        print("No case exceeds 1e-2 on any element.")
 
 
 if __name__ == "__main__":

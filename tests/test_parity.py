@@ -71,7 +71,7 @@ def _run_full(name, B, Nq, Nk, Hq, Hkv, d, causal, seed, dtype=torch.bfloat16, k
     o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
     torch.cuda.synchronize()
     O_ref, L_ref = attention_ref(q, k, v, causal, scale)
-    _compare(name, o, lse, O_ref, L_ref)
+    _compare(f"{name}/{'causal' if causal else 'noncausal'}", o, lse, O_ref, L_ref)
 
 
 # ---------------------------------------------------------------- every-row comparisons
