@@ -23,7 +23,7 @@ import math
 
 from . import _lib
 
-__all__ = ["forward", "forward_fp8", "forward_splitkv", "num_splits", "backward", "forward_varlen",
+__all__ = ["forward", "set_grid_order", "forward_fp8", "forward_splitkv", "num_splits", "backward", "forward_varlen",
            "forward_paged", "var_num_splits", "check_args", "FaError"]
 
 
@@ -124,6 +124,15 @@ def forward_fp8(q, k, v, q_scale: float = 1.0, k_scale: float = 1.0, v_scale: fl
     if rc != 0:
         _raise(rc)
     return out, lse
+
+
+def set_grid_order(mul: int = 0, add: int = 0) -> None:
+    """Grid order of every later launch in this process (testing hook for races between
+    workgroups): workgroup i takes work item (i * m + add) mod n, m the first value >= mul mod n
+    coprime with the grid size n; (0, 0) is the natural order."""
+    rc = _lib.load().fa_set_grid_order(int(mul) & 0xFFFFFFFF, int(add) & 0xFFFFFFFF)
+    if rc:
+        _raise(rc)
 
 
 def num_splits(B, Nq, Nk, Hq, d, causal=False) -> int:

@@ -109,6 +109,8 @@ def load():
         lib.fa_fwd_check.restype = _I
         lib.fa_strerror.argtypes = [_I]
         lib.fa_strerror.restype = ctypes.c_char_p
+        lib.fa_set_grid_order.argtypes = [ctypes.c_uint, ctypes.c_uint]
+        lib.fa_set_grid_order.restype = _I
         _lib = lib
     return _lib
 

@@ -46,6 +46,7 @@ struct BwdParams {
                 // zero_scores is set
   float scale;  // the signed scale (dQ = scale dS K, dK = scale dS^T Q)
   int zero_scores;  // scale is zero (or below the normal range): every score is exactly 0
+  unsigned order_mul, order_add;  // grid order (testing hook), as in FwdParams
 };
 
 template <int D>
@@ -131,9 +132,10 @@ bwd_dq_kernel(BwdParams p) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   // causal: the last query tiles see the most keys; they start first (longest-first), with
   // consecutive blocks on consecutive heads
+  const unsigned bid = (unsigned)work_item(p.order_mul, p.order_add);
   const int nbh = p.B * p.Hq;
-  const int bh = CAUSAL ? (int)(blockIdx.x % nbh) : (int)(blockIdx.x / p.ntile);
-  const int qt = CAUSAL ? p.ntile - 1 - (int)(blockIdx.x / nbh) : (int)(blockIdx.x % p.ntile);
+  const int bh = CAUSAL ? (int)(bid % nbh) : (int)(bid / p.ntile);
+  const int qt = CAUSAL ? p.ntile - 1 - (int)(bid / nbh) : (int)(bid % p.ntile);
   const int b = bh / p.Hq, hq = bh % p.Hq, kvh = hq / p.group;
   const int Nq = p.Nq, Nk = p.Nk;
   const int q_wg0 = qt * BR, qw0 = q_wg0 + wave * 32, q_lane = qw0 + l32;
@@ -294,9 +296,10 @@ bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   // causal: the first key tiles are seen by the most queries; they start first
+  const unsigned bid = (unsigned)work_item(p.order_mul, p.order_add);
   const int nbk = p.B * p.Hkv;
-  const int bk = CAUSAL ? (int)(blockIdx.x % nbk) : (int)(blockIdx.x / p.ntile);
-  const int kt = CAUSAL ? (int)(blockIdx.x / nbk) : (int)(blockIdx.x % p.ntile);
+  const int bk = CAUSAL ? (int)(bid % nbk) : (int)(bid / p.ntile);
+  const int kt = CAUSAL ? (int)(bid / nbk) : (int)(bid % p.ntile);
   const int b = bk / p.Hkv, kvh = bk % p.Hkv;
   const int Nq = p.Nq, Nk = p.Nk;
   const int k_wg0 = kt * BK, kw0 = k_wg0 + wave * 32, k_lane = kw0 + l32;

@@ -5,6 +5,8 @@
 
 #include <climits>
 #include <algorithm>
+#include <atomic>
+#include <numeric>
 #include <mutex>
 #include <cfloat>
 #include <cmath>
@@ -42,21 +44,41 @@ int noalloc_scratch(void** out) {
   return FA_OK;
 }
 
+// Grid order set by fa_set_grid_order (0: natural), read at each launch.
+std::atomic<unsigned> g_order_mul{0}, g_order_add{0};
+
+// The grid-order parameters of one launch of n workgroups: workgroup i takes item
+// (i * mul + add) mod n, with mul the first value >= the requested one (mod n; 1 for 0) that is
+// coprime with n, so that the map is a permutation. (0, 0) in the natural order.
+template <class P>
+P ordered(P prm, unsigned n) {
+  prm.order_mul = prm.order_add = 0;
+  const unsigned m = g_order_mul.load(std::memory_order_relaxed);
+  if (m == 0 || n == 0) return prm;
+  unsigned s = std::max(m % n, 1u);
+  while (std::gcd(s, n) != 1u) s = s + 1 < n ? s + 1 : 1u;  // ends at the latest at 1
+  prm.order_mul = s;
+  prm.order_add = g_order_add.load(std::memory_order_relaxed) % n;
+  return prm;
+}
+
 template <int D, bool CAUSAL, class T, int VM, int WV = fa::TileCfg<D>::NW>
 int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
   using L = fa::Layout<D, WV>;
   // the kernel's K/V buffers are static LDS (L::LDS bytes, within gfx950's 160 KB per CU)
-  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, T, VM, WV>), dim3(grid), dim3(L::NW * 64), 0, stream, prm);
+  hipLaunchKernelGGL((fa::fwd_kernel<D, CAUSAL, T, VM, WV>), dim3(grid), dim3(L::NW * 64), 0, stream,
+                     ordered(prm, (unsigned)grid));
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   if (VM == 2) {  // split-KV: merge the partials
     const size_t threads = (size_t)prm.B * prm.Hq * prm.Nq * (D / 8);
-    hipLaunchKernelGGL((fa::fwd_combine<D, T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, prm);
+    const unsigned g = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL((fa::fwd_combine<D, T>), dim3(g), dim3(256), 0, stream, ordered(prm, g));
     if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   }
   if (VM == 3) {  // variable-length split-KV: merge the partials of the packed rows
     const size_t threads = (size_t)prm.Hq * prm.total_q * (D / 8);
-    hipLaunchKernelGGL((fa::fwd_combine_var<D, T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                       prm);
+    const unsigned g = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL((fa::fwd_combine_var<D, T>), dim3(g), dim3(256), 0, stream, ordered(prm, g));
     if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   }
   return FA_OK;
@@ -116,7 +138,8 @@ void clear_extras(fa::FwdParams& prm) {
 template <int D, bool CAUSAL>
 int launch_fp8(const fa::FwdParams& prm, hipStream_t stream) {
   const int grid = prm.B * prm.Hq * prm.nqt;
-  hipLaunchKernelGGL((fa::fwd_fp8_kernel<D, CAUSAL>), dim3(grid), dim3(fa::Fp8Cfg<D>::NW * 64), 0, stream, prm);
+  hipLaunchKernelGGL((fa::fwd_fp8_kernel<D, CAUSAL>), dim3(grid), dim3(fa::Fp8Cfg<D>::NW * 64), 0, stream,
+                     ordered(prm, (unsigned)grid));
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -178,8 +201,9 @@ int check(const void* q, const void* k, const void* v, const void* o, const floa
 template <bool CAUSAL, class T>
 int launch_hd512(fa::FwdParams& prm, hipStream_t stream) {
   prm.nqt = (prm.Nq + fa::Hd512::BR - 1) / fa::Hd512::BR;
-  hipLaunchKernelGGL((fa::fwd_hd512_kernel<CAUSAL, T>), dim3(prm.B * prm.Hq * prm.nqt), dim3(fa::Hd512::NW * 64), 0,
-                     stream, prm);
+  const unsigned grid = (unsigned)(prm.B * prm.Hq * prm.nqt);
+  hipLaunchKernelGGL((fa::fwd_hd512_kernel<CAUSAL, T>), dim3(grid), dim3(fa::Hd512::NW * 64), 0, stream,
+                     ordered(prm, grid));
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -388,12 +412,12 @@ int launch_bwd(const fa::BwdParams& base, hipStream_t stream) {
   constexpr int NW = fa::BwdCfg<D>::NW, BR = NW * 32;
   fa::BwdParams prm = base;
   prm.ntile = (prm.Nq + BR - 1) / BR;
-  hipLaunchKernelGGL((fa::bwd_dq_kernel<D, CAUSAL, T>), dim3(prm.B * prm.Hq * prm.ntile), dim3(NW * 64), 0,
-                     stream, prm);
+  const unsigned gq = (unsigned)(prm.B * prm.Hq * prm.ntile);
+  hipLaunchKernelGGL((fa::bwd_dq_kernel<D, CAUSAL, T>), dim3(gq), dim3(NW * 64), 0, stream, ordered(prm, gq));
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   prm.ntile = (prm.Nk + BR - 1) / BR;
-  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<D, CAUSAL, T>), dim3(prm.B * prm.Hkv * prm.ntile), dim3(NW * 64), 0,
-                     stream, prm);
+  const unsigned gk = (unsigned)(prm.B * prm.Hkv * prm.ntile);
+  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<D, CAUSAL, T>), dim3(gk), dim3(NW * 64), 0, stream, ordered(prm, gk));
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -604,6 +628,12 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
   if (st != FA_OK) return st;
   return run_bwd<fa::Bf16>(q, k, v, o, lse, dout, dq, dk, dv, ws, sizeof(scratch), B, Nq, Nk, Hq, Hkv, d, causal,
                            scale, stream);
+}
+
+int fa_set_grid_order(unsigned mul, unsigned add) {
+  g_order_add.store(add, std::memory_order_relaxed);
+  g_order_mul.store(mul, std::memory_order_relaxed);
+  return FA_OK;
 }
 
 const char* fa_strerror(int code) {

@@ -59,7 +59,7 @@ fwd_hd512_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int pair = wave >> 1, half = wave & 1;
   int bh, qt;
-  decode_block<CAUSAL, false>(blockIdx.x, p, bh, qt);
+  decode_block<CAUSAL, false>(work_item(p.order_mul, p.order_add), p, bh, qt);
   const int b = bh / p.Hq, hq = bh - b * p.Hq, kvh = hq / p.group;
   const int Nq = p.Nq, Nk = p.Nk;
   const int q_wg0 = qt * BR, qw0 = q_wg0 + pair * 32, q_lane = qw0 + l32;

@@ -152,7 +152,18 @@ struct FwdParams {
   int splits, tps;
   // fp8 inputs (fwd_fp8_kernel): O is multiplied by v_scale; q and k scales are folded into c
   float v_scale;
+  // grid order (a testing hook): with order_mul != 0, workgroup i works on item
+  // (i * order_mul + order_add) mod n of a grid of n workgroups; the host keeps order_mul
+  // coprime with n, so this permutes the items. 0: item i.
+  unsigned order_mul, order_add;
 };
+
+// This workgroup's work item: blockIdx.x, or its image under the grid-order permutation. The
+// branch is uniform and taken once per workgroup.
+__device__ __forceinline__ int work_item(unsigned mul, unsigned add) {
+  if (mul == 0) return (int)blockIdx.x;
+  return (int)(((unsigned long long)blockIdx.x * mul + add) % gridDim.x);
+}
 
 template <bool V> struct BoolC { static constexpr bool value = V; };
 template <int V> struct IntC { static constexpr int value = V; };
@@ -353,19 +364,20 @@ fwd_kernel(FwdParams p) {
   const int hh = lane >> 5;
 
   int bh, qt, split = 0;
+  const int bid = work_item(p.order_mul, p.order_add);
   if constexpr (SPLITK) {
     // all blocks of split 0 first, then split 1, ...; within a split the order without splits
     const int per = p.B * p.Hq * p.nqt;
-    split = blockIdx.x / per;
-    decode_block<CAUSAL || VAR, VAR>(blockIdx.x - split * per, p, bh, qt);
+    split = bid / per;
+    decode_block<CAUSAL || VAR, VAR>(bid - split * per, p, bh, qt);
   } else if constexpr (VAR) {
     if (p.B <= 64) {
-      if (!decode_block_lpt<L::BR, L::BC, CAUSAL>(blockIdx.x, p, bh, qt)) return;
+      if (!decode_block_lpt<L::BR, L::BC, CAUSAL>(bid, p, bh, qt)) return;
     } else {
-      decode_block<true, true>(blockIdx.x, p, bh, qt);
+      decode_block<true, true>(bid, p, bh, qt);
     }
   } else {
-    decode_block<CAUSAL || VAR, VAR>(blockIdx.x, p, bh, qt);
+    decode_block<CAUSAL || VAR, VAR>(bid, p, bh, qt);
   }
   const int b = bh / p.Hq;
   const int hq = bh - b * p.Hq;
@@ -1045,7 +1057,7 @@ __global__ void __launch_bounds__(256) fwd_combine(FwdParams p) {
   using x2 = typename T::x2;
   constexpr int G = D / 8;
   const size_t rows = (size_t)p.B * p.Hq * p.Nq;
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t idx = (size_t)work_item(p.order_mul, p.order_add) * 256 + threadIdx.x;
   if (idx >= rows * G) return;
   const size_t r = idx / G;  // (b*Hq + h) * Nq + i
   const int g = (int)(idx - r * G);
@@ -1085,7 +1097,7 @@ template <int D, class T>
 __global__ void __launch_bounds__(256) fwd_combine_var(FwdParams p) {
   constexpr int G = D / 8;
   const size_t rows = (size_t)p.Hq * p.total_q;
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t idx = (size_t)work_item(p.order_mul, p.order_add) * 256 + threadIdx.x;
   if (idx >= rows * G) return;
   const size_t r = idx / G;  // h * total_q + i
   const int g = (int)(idx - r * G);

@@ -239,6 +239,16 @@ int fa_fwd_paged_splitkv_f16(const void* q, const void* k_cache, const void* v_c
                              int max_pages, int Hq, int Hkv, int d, int causal, float scale,
                              int num_splits, void* stream);
 
+/* Grid order, for tests that look for races between workgroups (a scheduling race shows up as
+ * a result that depends on the order in which workgroups run). After fa_set_grid_order(mul,
+ * add) with mul != 0, every later launch of this library in the process (forward, split-KV
+ * merge, fp8, head dim 512, backward) maps workgroup i of a grid of n workgroups to work item
+ * (i * m + add mod n) mod n, where m is the first value >= max(mul mod n, 1) coprime with n: a
+ * permutation of the work items, under which every result must stay bitwise the same.
+ * fa_set_grid_order(0, 0) restores the natural order (item i), which is the default. The
+ * setting is process-wide and read at launch; no HIP call is made. Returns FA_OK. */
+int fa_set_grid_order(unsigned mul, unsigned add);
+
 /* Static, NUL-terminated description of an fa_status code (never NULL). */
 const char* fa_strerror(int code);
 

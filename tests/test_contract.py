@@ -39,7 +39,7 @@ def test_library_exports_every_header_symbol():
                           "fa_fwd_splitkv_workspace_bytes", "fa_fwd_num_splits", "fa_fwd_fp8",
                           "fa_fwd_var_splitkv_workspace_bytes", "fa_fwd_varlen_splitkv",
                           "fa_fwd_varlen_splitkv_f16", "fa_fwd_paged_splitkv", "fa_fwd_paged_splitkv_f16",
-                          "fa_fwd_var_num_splits", "fa_bwd_noalloc"}
+                          "fa_fwd_var_num_splits", "fa_bwd_noalloc", "fa_set_grid_order"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -407,3 +407,10 @@ def test_var_num_splits_choice():
     assert fa.var_num_splits(4, 1, 512, 8, 256) == 0             # short caches: 16 tiles
     assert 2 <= fa.var_num_splits(4, 1, 2048, 8, 256) < 8        # 64 tiles
     assert fa.var_num_splits(4, 1, 2048, 8, 512) == 0            # unsupported head dim
+
+
+def test_grid_order_setter_makes_no_hip_call():
+    # a host-side setting only: returns FA_OK without a GPU, any values
+    lib = _lib.load()
+    for mul, add in ((7, 3), (0xFFFFFFFF, 0xFFFFFFFF), (0, 0)):
+        assert lib.fa_set_grid_order(mul, add) == _lib.FA_OK
