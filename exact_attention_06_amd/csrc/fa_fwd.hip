@@ -99,20 +99,26 @@ void set_scale(P& prm, float scale) {
 // hd128 takes the 4-wave workgroup when the 8-wave grid (without splits; for
 // variable-length batches the grid sized by the longest query sequence) has at most this many
 // workgroups, one per CU (measured on MI355X: +14-30% on causal shapes with 64-256
-// workgroups, 1-4% slower on full grids). Every form decides alike, so that one sequence
+// workgroups, 1-4% slower on full grids), and for causal GQA batches (query heads sharing a
+// K/V head) of at most kGqaCausalN4 query rows (measured: +6-12% at N = 1k and 2k with 2 and 4
+// query heads per K/V head, where the second K/V stream per CU stays in L2; the same form lost
+// 3-8% on causal batches without GQA). Every form decides alike, so that one sequence
 // through the variable-length path and the dense path, or one split and none, take the same
 // kernel configuration and agree bit for bit.
 constexpr int kSmallGrid128 = 256;
+constexpr int kGqaCausalN4 = 2048;
 
-bool use_4wave(int B, int Nq, int Hq, int d) {
+bool use_4wave(const fa::FwdParams& prm, int d, int causal) {
   const int64_t BR8 = fa::Layout<128>::BR;
-  return d == 128 && (int64_t)B * Hq * ((Nq + BR8 - 1) / BR8) <= kSmallGrid128;
+  if (d != 128) return false;
+  if ((int64_t)prm.B * prm.Hq * ((prm.Nq + BR8 - 1) / BR8) <= kSmallGrid128) return true;
+  return causal && prm.group >= 2 && prm.Nq <= kGqaCausalN4;
 }
 
 template <int VM, class T>
 int dispatch(fa::FwdParams& prm, int d, int causal, hipStream_t s) {
   const int splits = VM >= 2 ? prm.splits : 1;
-  if (d == 128 && use_4wave(prm.B, prm.Nq, prm.Hq, d)) {
+  if (use_4wave(prm, d, causal)) {
     constexpr int BR = fa::Layout<128, 4>::BR;
     prm.nqt = (prm.Nq + BR - 1) / BR;
     const int grid = prm.B * prm.Hq * prm.nqt * splits;
