@@ -62,6 +62,29 @@ P ordered(P prm, unsigned n) {
   return prm;
 }
 
+// The merge kernel with the split count as a compile-time constant (2-8: all loads issued
+// together) or read at run time (any other count).
+template <int D, class T, bool VAR, int NS>
+void launch_combine_ns(const fa::FwdParams& prm, unsigned g, hipStream_t stream) {
+  if (VAR)
+    hipLaunchKernelGGL((fa::fwd_combine_var<D, T, NS>), dim3(g), dim3(256), 0, stream, ordered(prm, g));
+  else
+    hipLaunchKernelGGL((fa::fwd_combine<D, T, NS>), dim3(g), dim3(256), 0, stream, ordered(prm, g));
+}
+template <int D, class T, bool VAR>
+void launch_combine(const fa::FwdParams& prm, unsigned g, hipStream_t stream) {
+  switch (prm.splits) {
+    case 2: launch_combine_ns<D, T, VAR, 2>(prm, g, stream); break;
+    case 3: launch_combine_ns<D, T, VAR, 3>(prm, g, stream); break;
+    case 4: launch_combine_ns<D, T, VAR, 4>(prm, g, stream); break;
+    case 5: launch_combine_ns<D, T, VAR, 5>(prm, g, stream); break;
+    case 6: launch_combine_ns<D, T, VAR, 6>(prm, g, stream); break;
+    case 7: launch_combine_ns<D, T, VAR, 7>(prm, g, stream); break;
+    case 8: launch_combine_ns<D, T, VAR, 8>(prm, g, stream); break;
+    default: launch_combine_ns<D, T, VAR, 0>(prm, g, stream); break;
+  }
+}
+
 template <int D, bool CAUSAL, class T, int VM, int WV = fa::TileCfg<D>::NW>
 int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
   using L = fa::Layout<D, WV>;
@@ -72,13 +95,13 @@ int launch(const fa::FwdParams& prm, int grid, hipStream_t stream) {
   if (VM == 2) {  // split-KV: merge the partials
     const size_t threads = (size_t)prm.B * prm.Hq * prm.Nq * (D / 8);
     const unsigned g = (unsigned)((threads + 255) / 256);
-    hipLaunchKernelGGL((fa::fwd_combine<D, T>), dim3(g), dim3(256), 0, stream, ordered(prm, g));
+    launch_combine<D, T, false>(prm, g, stream);
     if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   }
   if (VM == 3) {  // variable-length split-KV: merge the partials of the packed rows
     const size_t threads = (size_t)prm.Hq * prm.total_q * (D / 8);
     const unsigned g = (unsigned)((threads + 255) / 256);
-    hipLaunchKernelGGL((fa::fwd_combine_var<D, T>), dim3(g), dim3(256), 0, stream, ordered(prm, g));
+    launch_combine<D, T, true>(prm, g, stream);
     if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   }
   return FA_OK;

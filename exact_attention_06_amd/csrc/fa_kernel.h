@@ -1051,33 +1051,69 @@ fwd_kernel(FwdParams p) {
 // Merge of the split-KV partials (exact): for each row, LSE = ln sum_s exp(LSE_s) and
 // O = sum_s exp(LSE_s - LSE) * O_s, where O_s is split s's normalised output. A split that
 // saw no key of the row has LSE_s = -inf and weight 0. One thread per (row, 8 head-dim
-// values); the result goes to o [B, Nq, Hq, D] (T) and lse [B, Hq, Nq].
-template <int D, class T>
+// values). NS > 0: the split count is NS, known at compile time, and every split's LSE and
+// partial loads are issued before the first use (a loop over a run-time count issued them one
+// split after the other, each behind the previous one's wait: the merge was latency-bound);
+// NS = 0: any count. Both sum in split order, so they agree bit for bit.
+template <int D, int NS>
+__device__ __forceinline__ void merge_row(const FwdParams& p, size_t r, int g, size_t plane, float (&acc)[8],
+                                          float& m, float& sum) {
+  m = -__builtin_inff();
+  sum = 0.f;
+  if constexpr (NS > 0) {
+    float ls[NS];
+    f32x4 a[NS], bq[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      ls[s] = p.part_lse[s * plane + r];
+      const f32x4* po = (const f32x4*)(p.part_o + (s * plane + r) * D + 8 * g);
+      a[s] = po[0];
+      bq[s] = po[1];
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) m = __builtin_fmaxf(m, ls[s]);
+    // no branch on m (the loads above would sink behind it): with every LSE_s = -inf the
+    // weights are exp2(-inf) = 0 and the row stays empty, as in the loop below
+    const float mm = m == -__builtin_inff() ? 0.f : m;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float w = __builtin_amdgcn_exp2f((ls[s] - mm) * LOG2E);
+      sum += w;
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += w * a[s][e];
+        acc[4 + e] += w * bq[s][e];
+      }
+    }
+  } else {
+    for (int s = 0; s < p.splits; ++s) m = __builtin_fmaxf(m, p.part_lse[s * plane + r]);
+    if (m != -__builtin_inff()) {
+      for (int s = 0; s < p.splits; ++s) {
+        const float w = __builtin_amdgcn_exp2f((p.part_lse[s * plane + r] - m) * LOG2E);
+        sum += w;
+        const f32x4* po = (const f32x4*)(p.part_o + (s * plane + r) * D + 8 * g);
+        const f32x4 a = po[0], bq = po[1];
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += w * a[e];
+          acc[4 + e] += w * bq[e];
+        }
+      }
+    }
+  }
+}
+
+// Dense batches: partials [splits, B*Hq, Nq, D] and [splits, B*Hq, Nq]; the result goes to
+// o [B, Nq, Hq, D] (T) and lse [B, Hq, Nq].
+template <int D, class T, int NS>
 __global__ void __launch_bounds__(256) fwd_combine(FwdParams p) {
-  using x2 = typename T::x2;
   constexpr int G = D / 8;
   const size_t rows = (size_t)p.B * p.Hq * p.Nq;
   const size_t idx = (size_t)work_item(p.order_mul, p.order_add) * 256 + threadIdx.x;
   if (idx >= rows * G) return;
   const size_t r = idx / G;  // (b*Hq + h) * Nq + i
   const int g = (int)(idx - r * G);
-  const size_t plane = rows;  // rows per split
-  float m = -__builtin_inff();
-  for (int s = 0; s < p.splits; ++s) m = __builtin_fmaxf(m, p.part_lse[s * plane + r]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float sum = 0.f;
-  if (m != -__builtin_inff()) {
-    for (int s = 0; s < p.splits; ++s) {
-      const float w = __builtin_amdgcn_exp2f((p.part_lse[s * plane + r] - m) * LOG2E);
-      sum += w;
-      const f32x4* po = (const f32x4*)(p.part_o + (s * plane + r) * D + 8 * g);
-      const f32x4 a = po[0], bq = po[1];
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += w * a[e];
-        acc[4 + e] += w * bq[e];
-      }
-    }
-  }
+  float m, sum;
+  merge_row<D, NS>(p, r, g, rows, acc, m, sum);
   const float inv = sum > 0.f ? 1.0f / sum : 0.f;
   const size_t bhq = r / p.Nq;
   const int i = (int)(r - bhq * p.Nq);
@@ -1093,7 +1129,7 @@ __global__ void __launch_bounds__(256) fwd_combine(FwdParams p) {
 // The same merge for variable-length batches: partials [splits, Hq, total_q, D] and
 // [splits, Hq, total_q]; the result goes to o [total_q, Hq, D] (T) and lse [Hq, total_q].
 // A row whose splits all saw no key keeps O = 0 and LSE = -inf.
-template <int D, class T>
+template <int D, class T, int NS>
 __global__ void __launch_bounds__(256) fwd_combine_var(FwdParams p) {
   constexpr int G = D / 8;
   const size_t rows = (size_t)p.Hq * p.total_q;
@@ -1101,22 +1137,9 @@ __global__ void __launch_bounds__(256) fwd_combine_var(FwdParams p) {
   if (idx >= rows * G) return;
   const size_t r = idx / G;  // h * total_q + i
   const int g = (int)(idx - r * G);
-  float m = -__builtin_inff();
-  for (int s = 0; s < p.splits; ++s) m = __builtin_fmaxf(m, p.part_lse[s * rows + r]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float sum = 0.f;
-  if (m != -__builtin_inff()) {
-    for (int s = 0; s < p.splits; ++s) {
-      const float w = __builtin_amdgcn_exp2f((p.part_lse[s * rows + r] - m) * LOG2E);
-      sum += w;
-      const f32x4* po = (const f32x4*)(p.part_o + (s * rows + r) * D + 8 * g);
-      const f32x4 a = po[0], bq = po[1];
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += w * a[e];
-        acc[4 + e] += w * bq[e];
-      }
-    }
-  }
+  float m, sum;
+  merge_row<D, NS>(p, r, g, rows, acc, m, sum);
   const float inv = sum > 0.f ? 1.0f / sum : 0.f;
   const int h = (int)(r / p.total_q);
   const size_t i = r - (size_t)h * p.total_q;
