@@ -284,7 +284,7 @@ struct SplitRule {
 constexpr SplitRule kSplit128[] = {{-1, 0, 1}};
 constexpr SplitRule kSplit128Causal[] = {{64, 32, 2}, {128, 64, 3}};
 constexpr SplitRule kSplit256[] = {{64, 24, 3}, {128, 48, 3}};
-constexpr SplitRule kSplit256Causal[] = {{64, 32, 4}, {128, 64, 2}, {256, 128, 3}};
+constexpr SplitRule kSplit256Causal[] = {{64, 32, 4}, {128, 32, 2}, {256, 128, 3}};
 
 int num_splits(int B, int Nq, int Nk, int Hq, int d, int causal) {
   if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || (d != 128 && d != 256)) return 1;

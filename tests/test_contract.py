@@ -284,7 +284,7 @@ def test_num_splits_choice():
     assert fa.num_splits(1, 1024, 1024, 8, 256) == 3                 # 64 workgroups, 32 key tiles
     assert fa.num_splits(1, 1024, 1024, 8, 256, causal=True) == 4
     assert fa.num_splits(2, 1024, 1024, 8, 256) == 1                 # 128 workgroups, 32 key tiles
-    assert fa.num_splits(2, 1024, 1024, 8, 256, causal=True) == 1
+    assert fa.num_splits(2, 1024, 1024, 8, 256, causal=True) == 2    # 128 workgroups, causal
     assert fa.num_splits(1, 2048, 2048, 8, 256) == 3                 # 128 workgroups, 64 key tiles
     assert fa.num_splits(1, 2048, 2048, 8, 256, causal=True) == 2
     assert fa.num_splits(1, 4096, 4096, 8, 256) == 1
