@@ -125,17 +125,21 @@ void set_scale(P& prm, float scale) {
 // workgroups, 1-4% slower on full grids), and for causal GQA batches (query heads sharing a
 // K/V head) of at most kGqaCausalN4 query rows (measured: +6-12% at N = 1k and 2k with 2 and 4
 // query heads per K/V head, where the second K/V stream per CU stays in L2; the same form lost
-// 3-8% on causal batches without GQA). Every form decides alike, so that one sequence
-// through the variable-length path and the dense path, or one split and none, take the same
-// kernel configuration and agree bit for bit.
+// 3-8% on causal batches without GQA), and for non-causal batches of at most kNonCausalN4
+// query rows (measured: +2-4% at N = 512 and 1k, 8-64 batches of 16 heads, with and without
+// GQA; no change at N = 1k with 56 heads; at N = 2k the 8-wave form stays 1% ahead). Every
+// form decides alike, so that one sequence through the variable-length path and the dense
+// path, or one split and none, take the same kernel configuration and agree bit for bit.
 constexpr int kSmallGrid128 = 256;
 constexpr int kGqaCausalN4 = 2048;
+constexpr int kNonCausalN4 = 1024;
 
 bool use_4wave(const fa::FwdParams& prm, int d, int causal) {
   const int64_t BR8 = fa::Layout<128>::BR;
   if (d != 128) return false;
   if ((int64_t)prm.B * prm.Hq * ((prm.Nq + BR8 - 1) / BR8) <= kSmallGrid128) return true;
-  return causal && prm.group >= 2 && prm.Nq <= kGqaCausalN4;
+  if (!causal) return prm.Nq <= kNonCausalN4;
+  return prm.group >= 2 && prm.Nq <= kGqaCausalN4;
 }
 
 template <int VM, class T>
