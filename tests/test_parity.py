@@ -243,6 +243,21 @@ def test_deterministic_and_batch_independent():
     assert torch.equal(o1[1:2], o3) and torch.equal(l1[1:2], l3)
 
 
+def test_hd128_workgroup_forms_agree_bitwise():
+    # hd128 runs 8-wave (256-row) or 4-wave (128-row) workgroups; a wave owns 32 rows in both
+    # and, without a mask, takes the same tiles through the same iterations, so a batch entry
+    # computed in the 8-wave grid (8 batches x 8 heads x 5 tiles of 256 rows = 320 workgroups)
+    # equals the same entry computed alone in the 4-wave form (a grid of 40), bit for bit
+    q, k, v = W.make_qkv(8, 1100, 1100, 8, 8, 128, seed=54)
+    _say("[gpu] hd128 8-wave vs 4-wave form")
+    o1, l1 = fa.forward(q.cuda(), k.cuda(), v.cuda())
+    for b in (0, 5):
+        o2, l2 = fa.forward(q[b:b + 1].contiguous().cuda(), k[b:b + 1].contiguous().cuda(),
+                            v[b:b + 1].contiguous().cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(o1[b:b + 1], o2) and torch.equal(l1[b:b + 1], l2), b
+
+
 def test_python_layer_errors_on_gpu_tensors():
     q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError, match="head dim"):
