@@ -11,6 +11,11 @@
 // operand), so P's rounding largely cancels in O; the LSE uses the fp32 sum of unrounded p.
 //
 // CDNA4 mapping (same transposed form and softmax as the bf16 kernel, 64-key tiles):
+//   * hd128 runs the bf16 hd128 kernel's software pipeline: the softmax of tile j is issued
+//     between the score MFMAs of tile j+1, and the fp32 row sum of tile j and the row max of
+//     tile j+1 between the P.V MFMAs of tile j (two score buffers; 4-5% faster than one tile
+//     at a time at N >= 8k, bitwise the same O). hd256 has no registers for a second score
+//     buffer and takes one tile at a time;
 //   * an MFMA A or B operand is 32 bytes per lane: row (lane % 32), 32 k-values selected by
 //     lane / 32. Any k order works as long as A and B use the same one (the product sums
 //     over k); GEMM1 takes d = 64t + 32(lane/32) + byte, GEMM2 takes, for byte j = 8w + e of
@@ -279,6 +284,180 @@ fwd_fp8_kernel(FwdParams p) {
   };
 
   i32x8 pb = {};  // P rounded to e4m3 (B operand of O^T += V^T P^T), rewritten every tile
+  using F = BoolC<false>;
+  using U = BoolC<true>;
+  if constexpr (D == 128) {
+  // ---- software pipeline (as the bf16 hd128 loop): iteration j loads K(j+2) and V(j+1);
+  //      phase 1 issues the score MFMAs of tile j+1 with the softmax of tile j between them,
+  //      phase 2 the P.V MFMAs of tile j with the fp32 row sum of tile j and the row max of
+  //      tile j+1 (which decides the next rescale) between them.
+  auto load_k = [&](int tile, int buf) { load_tile(tile, kbase, buf ? k_lds1 : k_lds0, vo); };
+  auto load_v = [&](int tile, int buf) { load_tile(tile, vbase, buf ? v_lds1 : v_lds0, vo); };
+  auto rowmax = [&](const f32x16 (&s)[MT1]) -> float {
+    float mx = s[0][0];
+#pragma unroll
+    for (int mt = 0; mt < MT1; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[mt][r]);
+    return __builtin_fmaxf(mx, other_half(mx)) * c;
+  };
+  auto rescale_to = [&](const float mx) {
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
+      const float mnew = __builtin_fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+#pragma unroll
+      for (int i = 0; i <= MT2; ++i) acc[i] *= alpha;
+      lL *= alpha;
+      m_run = mnew;
+    }
+  };
+  load_k(0, 0);
+  load_v(0, 0);
+  if (ntiles > 1) load_k(1, 1);
+  tile_barrier();
+  f32x16 s_a[MT1], s_b[MT1];
+  gemm1(k_lds0, s_a);
+  tile_barrier();  // every wave has read K(0) before iteration 0 reloads its buffer
+  float mt_cur = 0.f;
+  // generic iteration (diagonal and tail tiles, and grids with a single tile)
+  auto iteration = [&](const int j, f32x16 (&sc)[MT1], f32x16 (&sn)[MT1], auto mask_tag) {
+    constexpr bool MASKED = decltype(mask_tag)::value;
+    const int par = j & 1;
+    const bool more_k = j + 2 < ntiles, more_v = j + 1 < ntiles;
+    if (more_k) load_k(j + 2, par);
+    if (more_v) load_v(j + 1, 1 - par);
+    const bool active = !MASKED || j < wtiles;
+    const bool next_active = MASKED ? (j + 1 < wtiles) : more_v;
+    if (active) {
+      if (MASKED) mask(j, sc);
+      rescale_to(rowmax(sc));
+      if (next_active) gemm1(par ? k_lds0 : k_lds1, sn);  // K(j+1): buffer 1 - par
+      softmax(sc, pb);
+      // keeps the all-ones operand in registers across tiles (the compiler rebuilt it with
+      // 7 moves per tile)
+      asm volatile("" : "+v"(ones));
+      gemm2(par ? v_lds1 : v_lds0, pb);
+    }
+    tile_barrier();
+  };
+  constexpr int N1 = KS1 * MT1;  // score MFMAs per tile
+  auto main_iteration = [&](const int j, f32x16 (&sc)[MT1], f32x16 (&sn)[MT1], auto par_tag) {
+    constexpr int PAR = decltype(par_tag)::value;  // j & 1
+    if (j + 2 < ntiles) load_k(j + 2, PAR);
+    load_v(j + 1, 1 - PAR);
+    rescale_to(mt_cur);
+    const float negm = -m_run;
+    const uint8_t* kl = PAR ? k_lds0 : k_lds1;  // K(j+1): buffer 1 - PAR
+    const uint8_t* vl = PAR ? v_lds1 : v_lds0;  // V(j): buffer PAR
+    auto kfrag = [&](const int i) -> i32x8 {
+      const int t = i / MT1, mt = i % MT1;
+      const int o0 = 16 * ((4 * t + 2 * hh) ^ fk), o1 = 16 * ((4 * t + 2 * hh + 1) ^ fk);
+      const uint8_t* rp = kl + k_rd + mt * 32 * ROW;
+      const u32x4 lo = *(const u32x4*)(rp + o0);
+      const u32x4 hi = *(const u32x4*)(rp + o1);
+      i32x8 a;
+      for (int e = 0; e < 4; ++e) {
+        a[e] = (int)lo[e];
+        a[4 + e] = (int)hi[e];
+      }
+      return a;
+    };
+    auto vfrag = [&](const int md) -> i32x8 {
+      const uint8_t* base = vl + v_rd + ((32 * md) ^ v_x);
+      i32x8 a;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2*)(base + (32 * (w >> 1) + 16 * (w & 1)) * ROW));
+        a[2 * w] = r[0];
+        a[2 * w + 1] = r[1];
+      }
+      return a;
+    };
+    i32x8 kf[N1], vf[MT2];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < N1; ++i) {
+      if (i + PF < N1)
+        kf[i + PF] = kfrag(i + PF);
+      else
+        vf[i + PF - N1] = vfrag(i + PF - N1);
+      {
+        const int t = i / MT1, mt = i % MT1;
+        sn[mt] = mfma_fp8(kf[i], qf[t], t == 0 ? f32x16{} : sn[mt]);
+      }
+      // softmax of two 4-score groups of tile j (words 2w, 2w + 1 of P); p overwrites its score
+#pragma unroll
+      for (int g = 2 * i; g < 2 * i + 2; ++g) {
+        const int w = g >> 1, h = g & 1, mt = w >> 1, r = 8 * (w & 1) + 4 * h;
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][r + e], c, negm));
+          sc[mt][r + e] = pv[e];
+        }
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], pb[g], false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
+        pb[g] = word;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    asm volatile("" : "+v"(ones));
+    float mx = -__builtin_inff(), sum0 = 0.f, sum1 = 0.f;
+    constexpr int VPS = 16 * MT1 / MT2;  // p values summed (and next-tile scores maxed) per step
+#pragma unroll
+    for (int md = 0; md < MT2; ++md) {
+      if (md + PF < MT2) vf[md + PF] = vfrag(md + PF);
+      acc[md] = mfma_fp8(vf[md], pb, acc[md]);
+#pragma unroll
+      for (int e = md * VPS; e < (md + 1) * VPS; ++e) {
+        if (e & 1)
+          sum1 += sc[e / 16][e % 16];
+        else
+          sum0 += sc[e / 16][e % 16];
+        mx = __builtin_fmaxf(mx, sn[e / 16][e % 16]);
+      }
+      asm volatile("" : "+v"(mx), "+v"(sum0), "+v"(sum1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    acc[MT2] = mfma_fp8(ones, pb, acc[MT2]);
+    lL += sum0 + sum1;
+    mx = __builtin_fmaxf(mx, other_half(mx));
+    mt_cur = mx * c;
+    tile_barrier();  // the loads of this iteration have landed; LDS reads of it are done
+  };
+  const int nmain = min(nfull, ntiles - 1);
+  int j = 0;
+  if (nmain > 0) {
+    mt_cur = rowmax(s_a);
+    main_iteration(0, s_a, s_b, IntC<0>{});
+    j = 1;
+    for (; j + 1 < nmain; j += 2) {
+      main_iteration(j, s_b, s_a, IntC<1>{});
+      main_iteration(j + 1, s_a, s_b, IntC<0>{});
+    }
+    if (j < nmain) {
+      main_iteration(j, s_b, s_a, IntC<1>{});
+      ++j;
+    }
+  }
+  // diagonal and tail tiles; the scores of tile j move to s_a first
+  if (j < ntiles && (j & 1)) {
+#pragma unroll
+    for (int mt = 0; mt < MT1; ++mt) s_a[mt] = s_b[mt];
+  }
+  for (; j < ntiles; ++j) {
+    iteration(j, s_a, s_b, U{});
+#pragma unroll
+    for (int mt = 0; mt < MT1; ++mt) s_a[mt] = s_b[mt];
+  }
+  } else {
+  // ---- hd256: one tile at a time (no registers for a second score buffer); the two
+  //      workgroups of a CU overlap each other
   auto iteration = [&](const int j, const int par, auto mask_tag) {
     constexpr bool MASKED = decltype(mask_tag)::value;
     if (j + 1 < ntiles) load_kv(j + 1, 1 - par);
@@ -287,17 +466,12 @@ fwd_fp8_kernel(FwdParams p) {
       gemm1(par ? k_lds1 : k_lds0, sc);
       if (MASKED) mask(j, sc);
       rescale(sc);
-      if constexpr (D != 128) pb = i32x8{};  // (a fresh value: nothing stays live across tiles)
+      pb = i32x8{};  // (a fresh value: nothing stays live across tiles)
       softmax(sc, pb);
-      // hd128: keeps the all-ones operand in registers across tiles (the compiler rebuilt it
-      // with 7 moves per tile)
-      if constexpr (D == 128) asm volatile("" : "+v"(ones));
       gemm2(par ? v_lds1 : v_lds0, pb);
     }
     tile_barrier();  // the loads of this iteration have landed; LDS reads of it are done
   };
-  using F = BoolC<false>;
-  using U = BoolC<true>;
   load_kv(0, 0);
   tile_barrier();
   int j = 0;
@@ -310,6 +484,8 @@ fwd_fp8_kernel(FwdParams p) {
     ++j;
   }
   for (; j < ntiles; ++j) iteration(j, j & 1, U{});
+
+  }
 
   // ---- epilogue: O = v_scale * O_acc / sum(rounded P); LSE from the fp32 sum of p
   lL += other_half(lL);
