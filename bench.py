@@ -349,18 +349,23 @@ def main():
             del qx, kx, vx
             for c in (False, True):
                 call = lambda: fa.forward_fp8(q8, k8, v8, sc[0], sc[1], sc[2], causal=c, scale=x.scale)
-                for _ in range(2):
+                # this section follows the short split-KV launches, during which the shader clock
+                # drops: 10 warm-up launches, then the mean of 3 repeats of the timed launches
+                for _ in range(10):
                     call()
                 torch.cuda.synchronize()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
                 n = max(1, args.sweep_steps)
-                e0.record()
-                for _ in range(n):
-                    call()
-                e1.record()
-                torch.cuda.synchronize()
-                m = e0.elapsed_time(e1) / n
+                reps = []
+                for _ in range(3):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(n):
+                        call()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    reps.append(e0.elapsed_time(e1) / n)
+                m = sum(reps) / len(reps)
                 t = x.flops(c) / (m * 1e-3) / 1e12
                 fp8.append({"workload": x.name, "causal": c, "ms": round(m, 4), "tflops": round(t, 1),
                             "frac_fp8_peak": round(t / PEAK_FP8_TFLOPS, 4)})
