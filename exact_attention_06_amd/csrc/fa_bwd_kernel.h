@@ -190,8 +190,10 @@ bwd_dq_kernel(BwdParams p) {
     if (j < wtiles) {
       const uint8_t* kl = PAR ? k_lds1 : k_lds0;
       const uint8_t* vl = PAR ? v_lds1 : v_lds0;
-      // S^T and dP^T, each as two alternating accumulators over the head dim
-      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+      // S^T and dP^T: one accumulator each (the two chains alternate, so neither MFMA waits
+      // for its predecessor; two alternating accumulators per product cost 32 registers and
+      // 32 adds per tile and ran 1-3% slower)
+      f32x16 s = f32x16{}, dp = f32x16{};
       {
         // step t: the K and V fragments of head-dim step t, read PF1 steps ahead
         x8 kf_[KS1], vf_[KS1];
@@ -205,17 +207,11 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int t = 0; t < KS1; ++t) {
           if (t + PF1 < KS1) rd(t + PF1);
-          if (t & 1) {
-            s1 = T::mfma(kf_[t], qf[t], s1);
-            p1 = T::mfma(vf_[t], df[t], p1);
-          } else {
-            s0 = T::mfma(kf_[t], qf[t], s0);
-            p0 = T::mfma(vf_[t], df[t], p0);
-          }
+          s = T::mfma(kf_[t], qf[t], s);
+          dp = T::mfma(vf_[t], df[t], dp);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      const f32x16 s = s0 + s1, dp = p0 + p1;
       // P^T, dS^T; key of register r: j*BT + 8(r/4) + 4hh + r%4; query q_lane
       const int k0 = j * BT;
       const int last = CAUSAL ? min(q_lane, Nk - 1) : Nk - 1;
@@ -369,8 +365,14 @@ bwd_dkdv_kernel(BwdParams p) {
     if (active) {
       const uint8_t* ql = q_lds[buf];
       const uint8_t* dl = d_lds[buf];
-      // S[q][k] and dP[q][k] (A = Q / dO rows from LDS, B = this lane's K / V)
-      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+      // S[q][k] and dP[q][k] (A = Q / dO rows from LDS, B = this lane's K / V). hd128: one
+      // accumulator each (+2-3% over two alternating ones per product, which cost 32 registers
+      // and 32 adds per tile); hd256 keeps two each: with one, the compiler's schedule of this
+      // kernel ran 10% slower non-causal (3% faster causal)
+      constexpr bool TWO_ACC = D == 256;
+      f32x16 s0 = f32x16{}, s1_ = f32x16{}, p0 = f32x16{}, p1_ = f32x16{};
+      f32x16& s1 = TWO_ACC ? s1_ : s0;
+      f32x16& p1 = TWO_ACC ? p1_ : p0;
       if constexpr (PF1 == 0) {
 #pragma unroll
         for (int t = 0; t < KS1; t += 2) {
@@ -406,7 +408,7 @@ bwd_dkdv_kernel(BwdParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      const f32x16 s = s0 + s1, dp = p0 + p1;
+      const f32x16 s = TWO_ACC ? s0 + s1_ : s0, dp = TWO_ACC ? p0 + p1_ : p0;
       // register r holds query q0 + 8(r/4) + 4hh + r%4 of this lane's key k_lane
       x8 pf[KS2], dsf[KS2];
 #pragma unroll
