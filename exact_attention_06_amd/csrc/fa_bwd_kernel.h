@@ -377,9 +377,10 @@ bwd_dkdv_kernel(BwdParams p) {
       const uint8_t* ql = q_lds[buf];
       const uint8_t* dl = d_lds[buf];
       // S[q][k] and dP[q][k] (A = Q / dO rows from LDS, B = this lane's K / V). hd128: one
-      // accumulator each (+2-3% over two alternating ones per product, which cost 32 registers
-      // and 32 adds per tile); hd256 keeps two each: with one, the compiler's schedule of this
-      // kernel ran 10% slower non-causal (3% faster causal)
+      // accumulator each (with the dq kernel's, +4% non-causal and +1% causal over two
+      // alternating ones per product, which cost 32 registers and 32 adds per tile); hd256
+      // keeps two each: with one, the compiler's schedule of this kernel ran 10% slower
+      // non-causal (3% faster causal)
       constexpr bool TWO_ACC = D == 256;
       f32x16 s0 = f32x16{}, s1_ = f32x16{}, p0 = f32x16{}, p1_ = f32x16{};
       f32x16& s1 = TWO_ACC ? s1_ : s0;

@@ -13,7 +13,7 @@
 // CDNA4 mapping (same transposed form and softmax as the bf16 kernel, 64-key tiles):
 //   * hd128 runs the bf16 hd128 kernel's software pipeline: the softmax of tile j is issued
 //     between the score MFMAs of tile j+1, and the fp32 row sum of tile j and the row max of
-//     tile j+1 between the P.V MFMAs of tile j (two score buffers; 4-5% faster than one tile
+//     tile j+1 between the P.V MFMAs of tile j (two score buffers; 3-6% faster than one tile
 //     at a time at N >= 8k, bitwise the same O). hd256 has no registers for a second score
 //     buffer and takes one tile at a time;
 //   * an MFMA A or B operand is 32 bytes per lane: row (lane % 32), 32 k-values selected by
