@@ -70,6 +70,10 @@ SMALL = [
     ("hd256",      1,  300,  2,  1,  256, 104),
     ("few",        1,  3,    2,  1,  128, 105),
     ("mid",        1,  1024, 4,  4,  256, 106),
+    # hd128 runs a software-pipelined tile loop: GQA over many main tiles, and an odd count
+    # of main tiles (31) followed by a 16-key tail tile
+    ("gqa_mid",    2,  1536, 8,  2,  128, 111),
+    ("long_odd",   1,  2000, 2,  1,  128, 112),
 ]
 
 
