@@ -73,6 +73,9 @@ CASES = [
     ("hd256",         1,  200,  200,  2,  1, 256, 64),
     ("few",           2,    3,    3,  2,  1, 128, 65),
     ("mid",           1, 1024, 1024,  4,  4, 128, 66),
+    # many key tiles that skip the mask in the dq kernel, then a ragged tail tile
+    ("ragged_long",   2, 1100, 1100,  4,  4, 128, 69),
+    ("gqa_long_256",  1, 1500, 1500,  8,  2, 256, 70),
 ]
 
 
