@@ -85,7 +85,7 @@ def test_fp8_all_rows(case, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
-@pytest.mark.parametrize("wname", ["hd128_N8192_mha", "hd256_N8192"])
+@pytest.mark.parametrize("wname", ["hd128_N8192_mha", "hd128_N8192_gqa4", "hd256_N8192"])
 def test_fp8_full_size_sampled_rows(wname, causal):
     w = W.by_name(wname)
     rows = [0, 1, 63, 64, 127, 128, 4095, 4096, w.N - 2, w.N - 1] + list(range(200, 8000, 1201))
