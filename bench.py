@@ -166,6 +166,8 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--only-fp8", action="store_true",
+                    help="besides the headline workload, run only the fp8 section; used to profile it")
     ap.add_argument("--only-variants", action="store_true",
                     help="besides the headline workload, run only the serving variants (packed and "
                          "paged prefill, paged decode); used to profile them")
@@ -245,7 +247,7 @@ def main():
     log(f"[bench] {w.name} causal={causal}: {ms:.3f} ms/step, {tflops:.1f} TFLOPS "
         f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS:.0f})")
 
-    rest = not args.no_sweep and not args.only_variants  # sweep, short-sequence and fp8 sections
+    rest = not args.no_sweep and not args.only_variants and not args.only_fp8  # sweep, short, fp8
     sweep = []
     if rest:
         pts = [x for x in W.hd128_sweep() + W.hd256_sweep() + [W.video()] + W.hd512_sweep()]
@@ -269,7 +271,7 @@ def main():
     # backward pass (gradients of sum(O * dO)); FLOPs counted as 2.5x the forward's
     # (five N x N x d products), the usual convention
     backward = []
-    if not args.no_backward and not args.only_variants:
+    if not args.no_backward and not args.only_variants and not args.only_fp8:
         for name in ("hd128_N8192_mha", "hd256_N8192"):
             x = W.by_name(name)
             qx, kx, vx = gpu_inputs(x, torch)
@@ -340,7 +342,7 @@ def main():
     # fp8 (e4m3) inputs, one dequantisation factor per tensor, bf16 output; priced against the
     # fp8 MFMA peak
     fp8 = []
-    if rest:
+    if rest or args.only_fp8:
         for name in ("hd128_N8192_mha", "hd256_N8192"):
             x = W.by_name(name)
             qx, kx, vx = gpu_inputs(x, torch)
@@ -377,7 +379,7 @@ def main():
     # serving variants: packed variable-length prefill, paged prefill, paged decode; each without
     # splits and, where the library picks a split count for its shape, split over the keys too
     variants = []
-    if not args.no_sweep or args.only_variants:
+    if (not args.no_sweep or args.only_variants) and not args.only_fp8:
         for x in W.bench_var_workloads():
             mq = max(x.seqlens_q)
             if x.paged:

@@ -94,7 +94,7 @@ def counter_values(pmc_dir, kernel_regex):
     return out
 
 
-def summarize(name, kernel_regex, flops, compulsory, trace_dir, pmc_dirs, skip):
+def summarize(name, kernel_regex, flops, compulsory, trace_dir, pmc_dirs, skip, peak=PEAK_BF16_TFLOPS):
     d = kernel_durations(trace_dir, kernel_regex)
     if len(d) <= skip:
         raise ValueError(f"{len(d)} dispatches of {kernel_regex!r}, fewer than --skip {skip} + 1")
@@ -103,7 +103,7 @@ def summarize(name, kernel_regex, flops, compulsory, trace_dir, pmc_dirs, skip):
            "median_ns_timed": statistics.median(timed), "min_ns_timed": min(timed), "max_ns_timed": max(timed),
            "avg_ns_all": statistics.fmean(d), "max_ns_all": max(d)}
     rec["achieved_tflops"] = flops / (rec["avg_ns_timed"] * 1e-9) / 1e12
-    rec["frac"] = rec["achieved_tflops"] / PEAK_BF16_TFLOPS
+    rec["frac"] = rec["achieved_tflops"] / peak
     counters = {}
     for pd in pmc_dirs:
         for cname, vals in counter_values(pd, kernel_regex).items():
@@ -130,7 +130,7 @@ def summarize(name, kernel_regex, flops, compulsory, trace_dir, pmc_dirs, skip):
     return rec
 
 
-def markdown(name, workload_desc, rec, cmds, skip, source_hash):
+def markdown(name, workload_desc, rec, cmds, skip, source_hash, peak=PEAK_BF16_TFLOPS, peak_label="bf16"):
     L = [f"# {name} on {workload_desc}", "",
          f"Kernel source hash (`kernel_source_hash`): `{source_hash}`. Commands (run from the repository root):", ""]
     L += ["    " + c for c in cmds]
@@ -142,7 +142,7 @@ def markdown(name, workload_desc, rec, cmds, skip, source_hash):
           f"{rec['max_ns_timed']} |",
           f"| all ({rec['dispatches']}) | {rec['avg_ns_all']:.0f} | | | {rec['max_ns_all']} |", "",
           f"Algorithmic work per launch / timed average duration = {rec['achieved_tflops']:.1f} TFLOP/s = "
-          f"{100 * rec['frac']:.1f}% of the {PEAK_BF16_TFLOPS:.0f} TFLOP/s dense bf16 peak."]
+          f"{100 * rec['frac']:.1f}% of the {peak:.0f} TFLOP/s dense {peak_label} peak."]
     if "hbm_bytes" in rec:
         c = rec["counters"]
         L += ["", "## HBM traffic (per timed launch, calibrated by a 1 GiB device copy)", "",
@@ -240,6 +240,9 @@ def main(argv=None):
     ap.add_argument("--cmd", action="append", default=[])
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic-json")
+    ap.add_argument("--peak-tflops", type=float, default=PEAK_BF16_TFLOPS,
+                    help="dense MFMA peak the kernel is priced against (fp8: 5000)")
+    ap.add_argument("--peak-label", default="bf16")
     a = ap.parse_args(argv)
     if a.launch:
         specs = []
@@ -257,12 +260,12 @@ def main(argv=None):
     w = W.by_name(a.workload)
     flops = w.flops(a.causal)
     compulsory = 2 * w.B * w.d * (2 * w.N * w.Hq + 2 * w.N * w.Hkv) + 4 * w.B * w.Hq * w.N
-    rec = summarize(a.name, a.kernel_regex, flops, compulsory, a.trace, a.pmc, a.skip)
+    rec = summarize(a.name, a.kernel_regex, flops, compulsory, a.trace, a.pmc, a.skip, a.peak_tflops)
     h = kernel_source_hash()
     desc = (f"{w.name} (B={w.B}, N={w.N}, Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, "
             f"{'causal' if a.causal else 'non-causal'})")
     with open(a.out, "w") as f:
-        f.write(markdown(a.name, desc, rec, a.cmd, a.skip, h))
+        f.write(markdown(a.name, desc, rec, a.cmd, a.skip, h, a.peak_tflops, a.peak_label))
     if a.traffic_json:
         db = json.load(open(a.traffic_json)) if os.path.exists(a.traffic_json) else {}
         e = {"workload": w.name, "causal": a.causal, "source_hash": h, "timed_dispatches": rec["timed"],
